@@ -1,0 +1,185 @@
+/*
+ * moe.h -- libmoe: the routed-expert mixture-of-experts FFN layer of a
+ * DeepSeek-V4-Flash-class model on one AMD MI355X (gfx950).
+ *
+ * The layer (ds4 / DwarfStar 4 pages): a full-precision router picks k of E
+ * routed experts per token; each routed expert is a SwiGLU FFN whose weights
+ * are 2-bit quantized -- an IQ2_XXS-class codebook format for up/gate and
+ * Q2_K for down -- or MXFP4; a bf16 shared expert is added to the weighted
+ * sum of the routed experts ("DS4 (DwarfStar 4): Chay DeepSeek V4 Flash
+ * Local voi Metal & CUDA", dibi8.com, "Cac Doi Moi Kien Truc Chinh" item 1;
+ * "DwarfStar: a focused local inference engine for DeepSeek V4 and GLM 5.2",
+ * hysenlabs.com, "Model support and quantization"; grapeot.me ds4 post,
+ * opening paragraphs, for hash MoE routing).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless stated.  Arrays are row-major and
+ *    contiguous.  bf16 and fp16 values are passed as their uint16 bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls validate their arguments on the host, enqueue kernels on
+ *    `stream` and return without synchronising; results are ready when the
+ *    stream reaches them.  No call allocates or frees memory: scratch space
+ *    is the caller's `ws` buffer, sized by the matching *_workspace query.
+ *  - Return value: MOE_OK, or a negative MOE_E* code with a message
+ *    available from moe_last_error() (thread-local).  Argument errors are
+ *    detected before anything is enqueued.  Device-side faults are not
+ *    reported by these calls.
+ *  - T == 0 (no tokens) is a valid no-op.
+ *  - Calls are reentrant; concurrent calls must use distinct ws buffers.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument: null pointer, shape, k, alignment */
+  MOE_EUNSUPPORTED = -2, /* valid but unsupported format / shape combination */
+  MOE_ENOSPC = -3,       /* workspace smaller than the *_workspace query */
+  MOE_EHIP = -4          /* the HIP runtime refused a launch */
+};
+
+/* Weight formats.  Blocking is along the row-major flattened [rows, cols]
+ * matrix of one expert; experts are stored one after another.
+ *  MOE_FMT_BF16  data: uint16 bf16 [E][rows][cols].
+ *  MOE_FMT_Q2K   data: 84-byte super-blocks of 256 consecutive weights,
+ *                {uint8 sc[16]; uint8 qs[64]; fp16 d; fp16 dmin}:
+ *                sub-block s = i/16 has scale sc[s]&15 and min sc[s]>>4,
+ *                q_i = (qs[i/4] >> 2*(i%4)) & 3, w_i = d*scale*q_i - dmin*min.
+ *                Requires rows*cols % 256 == 0; a block may span rows.
+ *  MOE_FMT_VQ2   2.0625-bit codebook format standing for the pages'
+ *                IQ2_XXS-class up/gate format: data: uint8 codes
+ *                [E][rows][cols/4]; scales: fp16 [E][rows][cols/256];
+ *                codebook: int8 [256][4];
+ *                w[n][k] = scale[n][k/256] * codebook[code[n][k/4]][k%4].
+ *                Requires cols % 256 == 0.
+ *  MOE_FMT_MXFP4 OCP MX v1.0 FP4: data: uint8 [E][rows][cols/2] E2M1
+ *                nibbles (even k in the low nibble); scales: uint8 E8M0
+ *                [E][rows][cols/32]; w = E2M1 * 2^(e-127).
+ *                Requires cols % 32 == 0. */
+enum { MOE_FMT_BF16 = 0, MOE_FMT_Q2K = 1, MOE_FMT_VQ2 = 2, MOE_FMT_MXFP4 = 3 };
+
+/* Routing modes.
+ *  MOE_ROUTE_SOFTMAX_TOPK: the k largest router logits (equal logits go to
+ *    the lower expert index; NaN ranks lowest), weights = softmax over the
+ *    k selected logits (they sum to 1).
+ *  MOE_ROUTE_HASH: expert j of token t is ((splitmix64(token_id[t]) + j)
+ *    mod 2^64) mod E, j = 0..k-1, where splitmix64(x) is the first output of
+ *    SplitMix64 seeded with x; weights = softmax over those k router logits. */
+enum { MOE_ROUTE_SOFTMAX_TOPK = 0, MOE_ROUTE_HASH = 1 };
+
+/* One projection of n_experts experts, each [rows, cols] (out x in). */
+typedef struct {
+  int32_t fmt, n_experts, rows, cols;
+  const void *data;        /* see MOE_FMT_*; 16-byte aligned */
+  const void *scales;      /* VQ2: fp16 plane; MXFP4: E8M0 plane; else NULL */
+  const int8_t *codebook;  /* VQ2: int8 [256][4]; else NULL */
+} moe_weights;
+
+/* One MoE FFN layer.  gate/up are [E][I][H], down is [E][H][I]; the shared
+ * expert (optional: NULL pointers or I_shared == 0) is bf16 [I_shared][H],
+ * [I_shared][H], [H][I_shared]; the router is bf16 [E][H]. */
+typedef struct {
+  int32_t H, I, E, k, I_shared, route_mode;
+  const uint16_t *w_router;
+  moe_weights gate, up, down;
+  const uint16_t *shared_gate, *shared_up, *shared_down;
+} moe_layer;
+
+/* Text of the last error on the calling thread ("" if none). */
+const char *moe_last_error(void);
+int moe_abi_version(void);
+
+/* ---------------------------------------------------------------------- */
+/* moe_route: router logits + expert selection.
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h], every product exact and
+ *   the sum accumulated in fp64, rounded once to fp32 (the router stays at
+ *   full precision).  Then MOE_ROUTE_SOFTMAX_TOPK or MOE_ROUTE_HASH selection.
+ * x: bf16 [T][H]; w_router: bf16 [E][H].
+ * logits_in: optional fp32 [T][E]; when given, the router GEMM is skipped
+ *   and these logits are used (x and w_router may then be NULL).
+ * token_ids: int64 [T], required for MOE_ROUTE_HASH, else ignored.
+ * topk_idx: int32 [T][k] out; topk_w: fp32 [T][k] out (softmax weights in
+ *   selection order); logits_out: optional fp32 [T][E] out.
+ * ws: scratch of moe_route_workspace(T, E) bytes (may be 0 when logits_out
+ *   or logits_in is given).  1 <= k <= min(E, 16); E <= 1024. */
+size_t moe_route_workspace(int T, int E);
+int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uint16_t *w_router,
+              const float *logits_in, const int64_t *token_ids, int32_t *topk_idx, float *topk_w,
+              float *logits_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_dispatch: bucket the T*k (token, choice) slots by expert, stable in
+ * slot order f = t*k + j (a counting sort by prefix sum):
+ *   expert_offsets[e] = number of slots routed to experts < e
+ *   (expert_offsets[E] = T*k); bucket e is rows [offsets[e], offsets[e+1])
+ *   listing its slots in ascending f:
+ *   sorted_slot[r] = f, sorted_token[r] = f / k, slot_pos[f] = r.
+ * topk_idx: int32 [T][k] with values in [0, E) (not checked on device).
+ * Outputs are int32: expert_offsets [E+1], the others [T*k]. */
+size_t moe_dispatch_workspace(int T, int E, int k);
+int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_offsets,
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_expert_ffn: SwiGLU FFN of each expert over its bucket of tokens:
+ *   for bucket row r of expert e, token t = sorted_token[r]:
+ *   y_rows[r] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),
+ * with the weights dequantized on the fly.  x: bf16 [T][H]; gate/up/down
+ * as in moe_layer (any of the formats; gate and up of one format).
+ * expert_offsets: int32 [E+1] and sorted_token: int32 [n_rows] from
+ *   moe_dispatch; expert_offsets == NULL means one dense expert (expert 0
+ *   of the weights) applied to all T tokens in order (n_rows == T,
+ *   sorted_token ignored) -- the shared expert.
+ * y_rows: fp32 [n_rows][H] out.
+ * Accumulation is fp32.  Small buckets (decode) run dequant-fused GEMVs;
+ * large ones a grouped GEMM on matrix cores. */
+size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
+                                int fmt_down);
+int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
+                   const moe_weights *up, const moe_weights *down, const int32_t *expert_offsets,
+                   const int32_t *sorted_token, int n_rows, float *y_rows, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_combine: the gather form of the weighted scatter-add:
+ *   out[t][n] = shared_y[t][n] + sum_j topk_w[t][j] * y_rows[slot_pos[t*k+j]][n]
+ * summed in j order in fp32.  shared_y: optional fp32 [T][H].
+ * out_f32: fp32 [T][H] out; out_bf16: optional bf16 [T][H] copy (RNE). */
+int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
+                const float *topk_w, const float *shared_y, float *out_f32, uint16_t *out_bf16,
+                void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_forward: the whole layer, out = shared(x) + sum_j w_j FFN_{e_j}(x),
+ * equal to moe_route -> moe_dispatch -> moe_expert_ffn (routed and shared)
+ * -> moe_combine, fused where that pays (few tokens: four kernels with no
+ * host round trip).
+ * logits_in / token_ids: as in moe_route.  out_f32: fp32 [T][H];
+ * out_bf16, topk_idx_out [T][k], topk_w_out [T][k]: optional outputs. */
+size_t moe_forward_workspace(const moe_layer *layer, int T);
+int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,
+                const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* moe_dequantize: weights [w0, w0+count) of expert `expert`'s row-major
+ * flattened matrix, decoded to fp32 with the same device decoders the FFN
+ * kernels use.  out: fp32 [count]. */
+int moe_dequantize(const moe_weights *w, int expert, int64_t w0, int64_t count, float *out,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_MOE_H */

@@ -1,0 +1,308 @@
+"""Python binding of libmoe (include/moe.h): argument marshalling only.
+
+Every entry point takes torch tensors that live on the GPU, passes their
+device pointers and the current HIP stream to the C ABI, and raises
+``MoeError`` on a non-OK status.  All computation happens in libmoe's HIP
+kernels; there is no fallback path.  torch supplies device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+FMT_BF16, FMT_Q2K, FMT_VQ2, FMT_MXFP4 = 0, 1, 2, 3
+ROUTE_SOFTMAX_TOPK, ROUTE_HASH = 0, 1
+OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libmoe error {code}: {msg}")
+        self.code = code
+
+
+class Weights(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("n_experts", C.c_int32), ("rows", C.c_int32),
+                ("cols", C.c_int32), ("data", C.c_void_p), ("scales", C.c_void_p),
+                ("codebook", C.c_void_p)]
+
+
+class Layer(C.Structure):
+    _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+                ("I_shared", C.c_int32), ("route_mode", C.c_int32), ("w_router", C.c_void_p),
+                ("gate", Weights), ("up", Weights), ("down", Weights),
+                ("shared_gate", C.c_void_p), ("shared_up", C.c_void_p),
+                ("shared_down", C.c_void_p)]
+
+
+_lib = None
+
+
+def build():
+    """Compile libmoe.so for gfx950 (hipcc)."""
+    from . import buildlib
+    return buildlib.build()
+
+
+def lib():
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmoe.so is not built ({LIB_PATH}); run "
+                              "routed_expert_ffn_router_amd.build()")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+        L.moe_last_error.restype = C.c_char_p
+        L.moe_abi_version.restype = i32
+        L.moe_route_workspace.restype = sz
+        L.moe_route_workspace.argtypes = [i32, i32]
+        L.moe_route.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dispatch_workspace.restype = sz
+        L.moe_dispatch_workspace.argtypes = [i32, i32, i32]
+        L.moe_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn_workspace.restype = sz
+        L.moe_expert_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.moe_expert_ffn.argtypes = [i32, i32, i32, vp, C.POINTER(Weights), C.POINTER(Weights),
+                                     C.POINTER(Weights), vp, vp, i32, vp, vp, sz, vp]
+        L.moe_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_forward_workspace.restype = sz
+        L.moe_forward_workspace.argtypes = [C.POINTER(Layer), i32]
+        L.moe_forward.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dequantize.argtypes = [C.POINTER(Weights), i32, i64, i64, vp, vp]
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def _check(rc):
+    if rc != OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+BF16 = (torch.bfloat16, torch.int16)  # bf16 values, or their bit patterns
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a GPU tensor")
+    ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+    if not ok:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------
+# weights on the device
+# --------------------------------------------------------------------------
+
+class DeviceProj:
+    """One projection of E experts in device memory (see include/moe.h)."""
+
+    def __init__(self, fmt, E, N, K, data, scales=None, codebook=None):
+        self.fmt, self.E, self.N, self.K = fmt, E, N, K
+        self.data, self.scales, self.codebook = data, scales, codebook
+        self.c = Weights(fmt, E, N, K, _ptr(data), _ptr(scales), _ptr(codebook))
+
+    @classmethod
+    def upload(cls, p, device="cuda", codebook=None):
+        """From a host projection with numpy fields fmt/E/N/K/data/scales/codebook."""
+        data = torch.from_numpy(p.data.reshape(-1).view("uint8").copy()).to(device)
+        scales = None
+        if p.scales is not None:
+            scales = torch.from_numpy(p.scales.reshape(-1).view("uint8").copy()).to(device)
+        cb = codebook
+        if cb is None and p.codebook is not None:
+            cb = torch.from_numpy(p.codebook.reshape(-1).view("uint8").copy()).to(device)
+        return cls(p.fmt, p.E, p.N, p.K, data, scales, cb)
+
+    def clone(self):
+        return DeviceProj(self.fmt, self.E, self.N, self.K, self.data.clone(),
+                          None if self.scales is None else self.scales.clone(), self.codebook)
+
+    def nbytes_per_expert(self):
+        n = self.data.numel() // self.E
+        if self.scales is not None:
+            n += self.scales.numel() // self.E
+        return n
+
+
+class DeviceLayer:
+    """A whole MoE layer in device memory, with its moe_layer descriptor."""
+
+    def __init__(self, H, I, E, k, route_mode, w_router, gate, up, down,
+                 shared_gate=None, shared_up=None, shared_down=None):
+        self.H, self.I, self.E, self.k, self.route_mode = H, I, E, k, route_mode
+        self.w_router, self.gate, self.up, self.down = w_router, gate, up, down
+        self.shared_gate, self.shared_up, self.shared_down = shared_gate, shared_up, shared_down
+        self.I_shared = 0 if shared_gate is None else shared_gate.shape[0]
+        self.c = Layer(H, I, E, k, self.I_shared, route_mode, _ptr(w_router), gate.c, up.c, down.c,
+                       _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down))
+
+    @classmethod
+    def upload(cls, layer, route_mode=ROUTE_SOFTMAX_TOPK, device="cuda"):
+        """From a host layer (fields spec, w_router, gate, up, down, shared_*, codebook)."""
+        s = layer.spec
+
+        def u16(a):
+            return None if a is None else torch.from_numpy(a.view("int16").copy()).to(device)
+
+        cb = None
+        if layer.codebook is not None:
+            cb = torch.from_numpy(layer.codebook.reshape(-1).view("uint8").copy()).to(device)
+        return cls(s.H, s.I, s.E, s.k, route_mode, u16(layer.w_router),
+                   DeviceProj.upload(layer.gate, device, cb if layer.gate.fmt == FMT_VQ2 else None),
+                   DeviceProj.upload(layer.up, device, cb if layer.up.fmt == FMT_VQ2 else None),
+                   DeviceProj.upload(layer.down, device, cb if layer.down.fmt == FMT_VQ2 else None),
+                   u16(layer.shared_gate), u16(layer.shared_up), u16(layer.shared_down))
+
+    def clone(self):
+        """An independent copy of every weight (distinct device memory)."""
+        cl = lambda t: None if t is None else t.clone()
+        return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, cl(self.w_router),
+                           self.gate.clone(), self.up.clone(), self.down.clone(),
+                           cl(self.shared_gate), cl(self.shared_up), cl(self.shared_down))
+
+    def with_route_mode(self, mode):
+        return DeviceLayer(self.H, self.I, self.E, self.k, mode, self.w_router, self.gate,
+                           self.up, self.down, self.shared_gate, self.shared_up, self.shared_down)
+
+    def forward_workspace(self, T):
+        return lib().moe_forward_workspace(C.byref(self.c), T)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def route(x, w_router, k, mode=ROUTE_SOFTMAX_TOPK, logits_in=None, token_ids=None,
+          want_logits=True):
+    """moe_route -> (topk_idx int32 [T,k], topk_w fp32 [T,k], logits fp32 [T,E] or None)."""
+    dev = (x if x is not None else logits_in).device
+    if logits_in is not None:
+        T, E = logits_in.shape
+        H = 0 if x is None else x.shape[1]
+    else:
+        T, H = x.shape
+        E = w_router.shape[0]
+    _dev(x, BF16, "x")
+    _dev(w_router, BF16, "w_router")
+    _dev(logits_in, torch.float32, "logits_in")
+    _dev(token_ids, torch.int64, "token_ids")
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lo = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    ws = None if want_logits else _ws(lib().moe_route_workspace(T, E), dev)
+    _check(lib().moe_route(mode, T, H, E, k, _ptr(x), _ptr(w_router), _ptr(logits_in),
+                           _ptr(token_ids), _ptr(idx), _ptr(w), _ptr(lo), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream()))
+    return idx, w, lo
+
+
+def dispatch(topk_idx, E):
+    """moe_dispatch -> (expert_offsets [E+1], sorted_token, sorted_slot, slot_pos) int32."""
+    _dev(topk_idx, torch.int32, "topk_idx")
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ss = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = _ws(lib().moe_dispatch_workspace(T, E, k), dev)
+    _check(lib().moe_dispatch(T, E, k, _ptr(topk_idx), _ptr(off), _ptr(st), _ptr(ss), _ptr(sp),
+                              _ptr(ws), ws.numel(), _stream()))
+    return off, st, ss, sp
+
+
+def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows=None):
+    """moe_expert_ffn -> y_rows fp32 [n_rows, H] (dense over x when offsets is None)."""
+    _dev(x, BF16, "x")
+    _dev(expert_offsets, torch.int32, "expert_offsets")
+    _dev(sorted_token, torch.int32, "sorted_token")
+    T, H = x.shape
+    I = gate.N
+    if n_rows is None:
+        n_rows = T if expert_offsets is None else sorted_token.numel()
+    y = torch.empty((n_rows, H), dtype=torch.float32, device=x.device)
+    ws = _ws(lib().moe_expert_ffn_workspace(T, n_rows, gate.E, H, I, gate.fmt, down.fmt), x.device)
+    _check(lib().moe_expert_ffn(T, H, I, _ptr(x), C.byref(gate.c), C.byref(up.c), C.byref(down.c),
+                                _ptr(expert_offsets), _ptr(sorted_token), n_rows, _ptr(y),
+                                _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def combine(y_rows, slot_pos, topk_w, shared_y=None, want_bf16=False):
+    """moe_combine -> (out fp32 [T, H], out bf16 bits [T, H] or None)."""
+    _dev(y_rows, torch.float32, "y_rows")
+    _dev(slot_pos, torch.int32, "slot_pos")
+    _dev(topk_w, torch.float32, "topk_w")
+    _dev(shared_y, torch.float32, "shared_y")
+    T, k = topk_w.shape
+    H = y_rows.shape[1]
+    out = torch.empty((T, H), dtype=torch.float32, device=y_rows.device)
+    ob = torch.empty((T, H), dtype=torch.int16, device=y_rows.device) if want_bf16 else None
+    _check(lib().moe_combine(T, H, k, _ptr(y_rows), _ptr(slot_pos), _ptr(topk_w), _ptr(shared_y),
+                             _ptr(out), _ptr(ob), _stream()))
+    return out, ob
+
+
+class Forward:
+    """moe_forward on a DeviceLayer with preallocated outputs and workspace."""
+
+    def __init__(self, layer, T, device="cuda", want_bf16=False):
+        self.layer, self.T = layer, T
+        self.out = torch.empty((T, layer.H), dtype=torch.float32, device=device)
+        self.out_bf16 = torch.empty((T, layer.H), dtype=torch.int16, device=device) if want_bf16 else None
+        self.idx = torch.empty((T, layer.k), dtype=torch.int32, device=device)
+        self.w = torch.empty((T, layer.k), dtype=torch.float32, device=device)
+        self.ws = _ws(layer.forward_workspace(T), device)
+
+    def __call__(self, x, logits_in=None, token_ids=None, layer=None):
+        L = self.layer if layer is None else layer
+        _dev(x, BF16, "x")
+        _dev(logits_in, torch.float32, "logits_in")
+        _dev(token_ids, torch.int64, "token_ids")
+        _check(lib().moe_forward(C.byref(L.c), self.T, _ptr(x), _ptr(logits_in), _ptr(token_ids),
+                                 _ptr(self.out), _ptr(self.out_bf16), _ptr(self.idx), _ptr(self.w),
+                                 _ptr(self.ws), self.ws.numel(), _stream()))
+        return self.out
+
+
+def forward(layer, x, logits_in=None, token_ids=None):
+    """moe_forward -> (out fp32 [T, H], topk_idx, topk_w)."""
+    f = Forward(layer, x.shape[0], x.device)
+    f(x, logits_in, token_ids)
+    return f.out, f.idx, f.w
+
+
+def dequantize(proj, expert=0, w0=0, count=None):
+    """moe_dequantize -> fp32 weights [w0, w0+count) of one expert's flattened matrix."""
+    if count is None:
+        count = proj.N * proj.K - w0
+    out = torch.empty(count, dtype=torch.float32, device=proj.data.device)
+    _check(lib().moe_dequantize(C.byref(proj.c), expert, w0, count, _ptr(out), _stream()))
+    return out

@@ -1,0 +1,424 @@
+// api.hip -- the C ABI of libmoe (include/moe.h): argument validation,
+// workspace carving and kernel sequencing.  Host code only.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "moe_internal.h"
+
+namespace moe {
+bool gemv_supported_k(int K);
+}
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_check(hipError_t e, const char *where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)             \
+  do {                            \
+    int rc_ = (expr);             \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Sequential carving of the caller's workspace (base == nullptr: sizing only).
+struct Carver {
+  uint8_t *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base(static_cast<uint8_t *>(b)) {}
+  template <class T>
+  T *take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T *r = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return r;
+  }
+  size_t size() const { return (off + 255) & ~size_t(255); }
+};
+
+int check_weights(const moe_weights *w, const char *name, int E, int N, int K) {
+  if (!w) return fail(MOE_EINVAL, "%s: null weights", name);
+  if (w->fmt < MOE_FMT_BF16 || w->fmt > MOE_FMT_MXFP4)
+    return fail(MOE_EUNSUPPORTED, "%s: unknown format %d", name, w->fmt);
+  if (w->n_experts != E || w->rows != N || w->cols != K)
+    return fail(MOE_EINVAL, "%s: shape [%d][%d][%d], expected [%d][%d][%d]", name, w->n_experts,
+                w->rows, w->cols, E, N, K);
+  if (!w->data) return fail(MOE_EINVAL, "%s: null data", name);
+  if (!aligned(w->data, 16)) return fail(MOE_EINVAL, "%s: data not 16-byte aligned", name);
+  const long long n = (long long)N * K;
+  switch (w->fmt) {
+    case MOE_FMT_BF16:
+      if (K % 8) return fail(MOE_EINVAL, "%s: bf16 needs cols %% 8 == 0", name);
+      break;
+    case MOE_FMT_Q2K:
+      if (n % 256) return fail(MOE_EINVAL, "%s: q2k needs rows*cols %% 256 == 0", name);
+      break;
+    case MOE_FMT_VQ2:
+      if (K % 256) return fail(MOE_EINVAL, "%s: vq2 needs cols %% 256 == 0", name);
+      if (!w->scales || !w->codebook)
+        return fail(MOE_EINVAL, "%s: vq2 needs scales and codebook", name);
+      if (!aligned(w->scales, 2) || !aligned(w->codebook, 4))
+        return fail(MOE_EINVAL, "%s: vq2 scales/codebook misaligned", name);
+      break;
+    case MOE_FMT_MXFP4:
+      if (K % 32) return fail(MOE_EINVAL, "%s: mxfp4 needs cols %% 32 == 0", name);
+      if (!w->scales) return fail(MOE_EINVAL, "%s: mxfp4 needs scales", name);
+      break;
+  }
+  return MOE_OK;
+}
+
+int check_route_args(int mode, int T, int E, int k) {
+  if (mode != MOE_ROUTE_SOFTMAX_TOPK && mode != MOE_ROUTE_HASH)
+    return fail(MOE_EINVAL, "unknown routing mode %d", mode);
+  if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "E = %d outside [1, 1024]", E);
+  if (k < 1 || k > E || k > 16) return fail(MOE_EINVAL, "k = %d outside [1, min(E, 16)]", k);
+  return MOE_OK;
+}
+
+int check_ffn_weights(int E, int H, int I, const moe_weights *gate, const moe_weights *up,
+                      const moe_weights *down) {
+  MOE_TRY(check_weights(gate, "gate", E, I, H));
+  MOE_TRY(check_weights(up, "up", E, I, H));
+  MOE_TRY(check_weights(down, "down", E, H, I));
+  if (gate->fmt != up->fmt) return fail(MOE_EUNSUPPORTED, "gate and up formats differ");
+  if (gate->fmt == MOE_FMT_VQ2 && gate->codebook != up->codebook)
+    return fail(MOE_EUNSUPPORTED, "vq2 gate and up must share one codebook");
+  if (!gemv_supported_k(H) || !gemv_supported_k(I))
+    return fail(MOE_EUNSUPPORTED, "H = %d / I = %d: supported sizes are 128, 256, 512 and "
+                "multiples 1, 2, 4, 8 of 1024", H, I);
+  return MOE_OK;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+WView bf16_view(const uint16_t *p, int N, int K) {
+  return WView{MOE_FMT_BF16, 1, N, K, reinterpret_cast<const uint8_t *>(p), nullptr, nullptr};
+}
+
+// ---------------------------------------------------------------------------
+// expert FFN workspace and sequence (shared by moe_expert_ffn and moe_forward)
+// ---------------------------------------------------------------------------
+
+struct FfnBufs {
+  int32_t *plan;
+  float *a;
+};
+
+FfnBufs carve_ffn(Carver &c, int n_rows, int E, int I, bool dense) {
+  FfnBufs b;
+  b.plan = dense ? nullptr : c.take<int32_t>(plan_ints(std::min(E, std::max(n_rows, 1))));
+  b.a = c.take<float>((size_t)std::max(n_rows, 1) * I);
+  return b;
+}
+
+int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView &u,
+            const WView &d, const int32_t *offsets, const int32_t *sorted_token, int n_rows,
+            float *y, const FfnBufs &b, hipStream_t s) {
+  if (!offsets) {
+    MOE_TRY(hip_check(launch_gateup_gemv(g, u, H, I, x, nullptr, T, nullptr, b.a, s), "gate/up"));
+    return hip_check(launch_down_gemv(d, H, I, b.a, nullptr, T, y, s), "down");
+  }
+  const int E = g.E;
+  const int max_active = std::min(E, n_rows);
+  MOE_TRY(hip_check(launch_plan_from_offsets(E, offsets, b.plan, s), "plan"));
+  MOE_TRY(hip_check(launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, sorted_token, b.a, s),
+                    "gate/up"));
+  return hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, y, s), "down");
+}
+
+// ---------------------------------------------------------------------------
+// forward: buffers
+// ---------------------------------------------------------------------------
+
+struct FwdBufs {
+  float *logits;
+  int32_t *idx;
+  float *w;
+  float *a_sh, *shared_y;
+  // small path
+  int32_t *plan, *sorted_token, *slot_pos;
+  float *row_w, *a, *y_rows;
+  // large path
+  int32_t *offsets, *sorted_slot;
+  void *dispatch_ws;
+  FfnBufs ffn;
+};
+
+bool fwd_small(const moe_layer *L, int T) { return (long long)T * L->k <= kSmallSlots; }
+
+FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool have_idx,
+                  bool have_w) {
+  FwdBufs b{};
+  const int E = L->E, k = L->k, H = L->H, I = L->I;
+  const size_t n = (size_t)T * k;
+  const bool shared = L->I_shared > 0 && L->shared_gate;
+  b.logits = have_logits ? nullptr : c.take<float>((size_t)T * E);
+  b.idx = have_idx ? nullptr : c.take<int32_t>(n);
+  b.w = have_w ? nullptr : c.take<float>(n);
+  if (shared) {
+    b.a_sh = c.take<float>((size_t)T * L->I_shared);
+    b.shared_y = c.take<float>((size_t)T * H);
+  }
+  if (fwd_small(L, T)) {
+    b.plan = c.take<int32_t>(plan_ints(std::min<size_t>(E, n)));
+    b.sorted_token = c.take<int32_t>(n);
+    b.slot_pos = c.take<int32_t>(n);
+    b.row_w = c.take<float>(n);
+    b.a = c.take<float>(n * I);
+    if (T > 1) b.y_rows = c.take<float>(n * H);
+  } else {
+    b.offsets = c.take<int32_t>(E + 1);
+    b.sorted_token = c.take<int32_t>(n);
+    b.sorted_slot = c.take<int32_t>(n);
+    b.slot_pos = c.take<int32_t>(n);
+    b.dispatch_ws = c.take<uint8_t>(dispatch_ws_bytes(T, E, k));
+    b.y_rows = c.take<float>(n * H);
+    b.ffn = carve_ffn(c, (int)n, E, I, false);
+  }
+  return b;
+}
+
+int check_layer(const moe_layer *L) {
+  if (!L) return fail(MOE_EINVAL, "null layer");
+  MOE_TRY(check_route_args(L->route_mode, 0, L->E, L->k));
+  if (L->H < 1 || L->I < 1) return fail(MOE_EINVAL, "bad H = %d / I = %d", L->H, L->I);
+  if (!L->w_router) return fail(MOE_EINVAL, "null router");
+  if (!aligned(L->w_router, 16) || L->H % 8) return fail(MOE_EINVAL, "router misaligned");
+  MOE_TRY(check_ffn_weights(L->E, L->H, L->I, &L->gate, &L->up, &L->down));
+  if (L->I_shared < 0) return fail(MOE_EINVAL, "I_shared < 0");
+  if (L->I_shared > 0 && L->shared_gate) {
+    if (!L->shared_up || !L->shared_down) return fail(MOE_EINVAL, "incomplete shared expert");
+    if (!aligned(L->shared_gate, 16) || !aligned(L->shared_up, 16) ||
+        !aligned(L->shared_down, 16))
+      return fail(MOE_EINVAL, "shared expert misaligned");
+    if (!gemv_supported_k(L->I_shared))
+      return fail(MOE_EUNSUPPORTED, "I_shared = %d unsupported", L->I_shared);
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+// =============================================================================
+// C ABI
+// =============================================================================
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+size_t moe_route_workspace(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  return ((size_t)T * E * sizeof(float) + 255) & ~size_t(255);
+}
+
+int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uint16_t *w_router,
+              const float *logits_in, const int64_t *token_ids, int32_t *topk_idx, float *topk_w,
+              float *logits_out, void *ws, size_t ws_bytes, void *stream) {
+  MOE_TRY(check_route_args(mode, T, E, k));
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !topk_w) return fail(MOE_EINVAL, "null topk outputs");
+  if (mode == MOE_ROUTE_HASH && !token_ids) return fail(MOE_EINVAL, "hash routing needs token_ids");
+  hipStream_t s = as_stream(stream);
+  const float *lsrc = logits_in;
+  if (!logits_in) {
+    if (!x || !w_router) return fail(MOE_EINVAL, "null x or router");
+    if (H < 8 || H % 8) return fail(MOE_EINVAL, "H = %d must be a positive multiple of 8", H);
+    if (!aligned(x, 16) || !aligned(w_router, 16)) return fail(MOE_EINVAL, "x/router misaligned");
+    float *dst = logits_out;
+    if (!dst) {
+      if (!ws || ws_bytes < moe_route_workspace(T, E))
+        return fail(MOE_ENOSPC, "route workspace: %zu bytes < %zu", ws_bytes,
+                    moe_route_workspace(T, E));
+      dst = static_cast<float *>(ws);
+    }
+    MOE_TRY(hip_check(launch_router_logits(T, H, E, x, w_router, dst, s), "router"));
+    lsrc = dst;
+  } else if (logits_out) {
+    MOE_TRY(hip_check(hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),
+                                     hipMemcpyDeviceToDevice, s),
+                      "logits copy"));
+  }
+  return hip_check(launch_select(mode, T, E, k, lsrc, token_ids, topk_idx, topk_w, nullptr,
+                                 nullptr, nullptr, nullptr, nullptr, nullptr, s),
+                   "select");
+}
+
+size_t moe_dispatch_workspace(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return (dispatch_ws_bytes(T, E, k) + 255) & ~size_t(255);
+}
+
+int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_offsets,
+                 int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
+                 size_t ws_bytes, void *stream) {
+  MOE_TRY(check_route_args(MOE_ROUTE_SOFTMAX_TOPK, T, E, k));
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !expert_offsets || !sorted_token || !sorted_slot || !slot_pos)
+    return fail(MOE_EINVAL, "null dispatch pointer");
+  if ((long long)T * k > (1ll << 30)) return fail(MOE_EINVAL, "T*k too large");
+  if (!ws || ws_bytes < moe_dispatch_workspace(T, E, k))
+    return fail(MOE_ENOSPC, "dispatch workspace: %zu bytes < %zu", ws_bytes,
+                moe_dispatch_workspace(T, E, k));
+  return hip_check(launch_dispatch(T, E, k, topk_idx, expert_offsets, sorted_token, sorted_slot,
+                                   slot_pos, ws, as_stream(stream)),
+                   "dispatch");
+}
+
+size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
+                                int fmt_down) {
+  (void)T, (void)H, (void)fmt_gate, (void)fmt_down;
+  if (n_rows < 0 || E < 1 || I < 1) return 0;
+  Carver c(nullptr);
+  carve_ffn(c, n_rows, E, I, false);
+  return c.size();
+}
+
+int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
+                   const moe_weights *up, const moe_weights *down, const int32_t *expert_offsets,
+                   const int32_t *sorted_token, int n_rows, float *y_rows, void *ws,
+                   size_t ws_bytes, void *stream) {
+  if (T < 0 || n_rows < 0) return fail(MOE_EINVAL, "negative T or n_rows");
+  if (!gate) return fail(MOE_EINVAL, "null gate");
+  const int E = gate->n_experts;
+  MOE_TRY(check_ffn_weights(E, H, I, gate, up, down));
+  if (T == 0 || n_rows == 0) return MOE_OK;
+  if (!x || !y_rows) return fail(MOE_EINVAL, "null x or y_rows");
+  if (!aligned(x, 16) || !aligned(y_rows, 16)) return fail(MOE_EINVAL, "x/y_rows misaligned");
+  const bool dense = expert_offsets == nullptr;
+  if (dense && n_rows != T) return fail(MOE_EINVAL, "dense call needs n_rows == T");
+  if (!dense && !sorted_token) return fail(MOE_EINVAL, "null sorted_token");
+  const size_t need = moe_expert_ffn_workspace(T, n_rows, E, H, I, gate->fmt, down->fmt);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ENOSPC, "expert_ffn workspace: %zu bytes < %zu", ws_bytes, need);
+  Carver c(ws);
+  FfnBufs b = carve_ffn(c, n_rows, E, I, dense);
+  return run_ffn(T, H, I, x, view_of(*gate), view_of(*up), view_of(*down), expert_offsets,
+                 sorted_token, n_rows, y_rows, b, as_stream(stream));
+}
+
+int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
+                const float *topk_w, const float *shared_y, float *out_f32, uint16_t *out_bf16,
+                void *stream) {
+  if (T < 0 || H < 1 || k < 1 || k > 16) return fail(MOE_EINVAL, "bad T/H/k");
+  if (T == 0) return MOE_OK;
+  if (H % 4) return fail(MOE_EINVAL, "H = %d must be a multiple of 4", H);
+  if (!y_rows || !slot_pos || !topk_w || !out_f32) return fail(MOE_EINVAL, "null combine pointer");
+  if (!aligned(y_rows, 16) || !aligned(out_f32, 16) || (shared_y && !aligned(shared_y, 16)) ||
+      (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "combine buffers misaligned");
+  return hip_check(launch_combine(T, H, k, y_rows, slot_pos, topk_w, shared_y, out_f32, out_bf16,
+                                  as_stream(stream)),
+                   "combine");
+}
+
+size_t moe_forward_workspace(const moe_layer *L, int T) {
+  if (!L || T < 0 || L->E < 1 || L->k < 1) return 0;
+  Carver c(nullptr);
+  carve_fwd(c, L, T, false, false, false);
+  return c.size();
+}
+
+int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
+                const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                void *stream) {
+  MOE_TRY(check_layer(L));
+  if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
+  if (T == 0) return MOE_OK;
+  if (!x || !out_f32) return fail(MOE_EINVAL, "null x or out");
+  if (!aligned(x, 16) || !aligned(out_f32, 16) || (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "x/out misaligned");
+  if (L->route_mode == MOE_ROUTE_HASH && !token_ids)
+    return fail(MOE_EINVAL, "hash routing needs token_ids");
+  const size_t need = moe_forward_workspace(L, T);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ENOSPC, "forward workspace: %zu bytes < %zu", ws_bytes, need);
+
+  hipStream_t s = as_stream(stream);
+  const int E = L->E, k = L->k, H = L->H, I = L->I, n = T * k;
+  Carver c(ws);
+  FwdBufs b = carve_fwd(c, L, T, false, false, false);
+  int32_t *idx = topk_idx_out ? topk_idx_out : b.idx;
+  float *w = topk_w_out ? topk_w_out : b.w;
+  const float *logits = logits_in;
+  if (!logits) {
+    MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
+    logits = b.logits;
+  }
+  const bool shared = L->I_shared > 0 && L->shared_gate;
+  if (shared) {
+    const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
+    const WView su = bf16_view(L->shared_up, L->I_shared, H);
+    const WView sd = bf16_view(L->shared_down, H, L->I_shared);
+    MOE_TRY(hip_check(launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, s),
+                      "shared gate/up"));
+    MOE_TRY(hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, s),
+                      "shared down"));
+  }
+  const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
+  if (fwd_small(L, T)) {
+    MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
+                                    b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
+                      "select"));
+    const int max_active = std::min(E, n);
+    MOE_TRY(hip_check(
+        launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s), "gate/up"));
+    if (T == 1)
+      return hip_check(launch_down_combine(d, H, I, T, b.a, b.plan, max_active, b.sorted_token,
+                                           b.row_w, b.shared_y, out_f32, out_bf16, s),
+                       "down+combine");
+    MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
+    return hip_check(
+        launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
+        "combine");
+  }
+  MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
+                                  nullptr, nullptr, nullptr, nullptr, nullptr, s),
+                    "select"));
+  MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
+                                    b.slot_pos, b.dispatch_ws, s),
+                    "dispatch"));
+  MOE_TRY(run_ffn(T, H, I, x, g, u, d, b.offsets, b.sorted_token, n, b.y_rows, b.ffn, s));
+  return hip_check(
+      launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
+      "combine");
+}
+
+int moe_dequantize(const moe_weights *w, int expert, int64_t w0, int64_t count, float *out,
+                   void *stream) {
+  if (!w) return fail(MOE_EINVAL, "null weights");
+  MOE_TRY(check_weights(w, "weights", w->n_experts, w->rows, w->cols));
+  if (expert < 0 || expert >= w->n_experts) return fail(MOE_EINVAL, "expert %d out of range", expert);
+  const int64_t per = (int64_t)w->rows * w->cols;
+  if (w0 < 0 || count < 0 || w0 + count > per) return fail(MOE_EINVAL, "range out of bounds");
+  if (count == 0) return MOE_OK;
+  if (!out) return fail(MOE_EINVAL, "null out");
+  return hip_check(launch_dequant(view_of(*w), expert, w0, count, out, as_stream(stream)),
+                   "dequantize");
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// moe_internal.h -- host-side launchers shared between the libmoe sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// A projection as the kernels see it.
+struct WView {
+  int fmt, E, N, K;
+  const uint8_t *data;
+  const uint8_t *scales;
+  const int8_t *codebook;
+};
+
+inline WView view_of(const moe_weights &w) {
+  return WView{w.fmt, w.n_experts, w.rows, w.cols, static_cast<const uint8_t *>(w.data),
+               static_cast<const uint8_t *>(w.scales), w.codebook};
+}
+
+// Byte offset of expert e's data / scales in a projection.
+__host__ __device__ inline size_t expert_data_bytes(int fmt, int N, int K) {
+  size_t n = (size_t)N * K;
+  switch (fmt) {
+    case MOE_FMT_BF16: return n * 2;
+    case MOE_FMT_Q2K: return n / 256 * 84;
+    case MOE_FMT_VQ2: return n / 4;
+    case MOE_FMT_MXFP4: return n / 2;
+  }
+  return 0;
+}
+__host__ __device__ inline size_t expert_scale_bytes(int fmt, int N, int K) {
+  size_t n = (size_t)N * K;
+  switch (fmt) {
+    case MOE_FMT_VQ2: return n / 256 * 2;
+    case MOE_FMT_MXFP4: return n / 32;
+  }
+  return 0;
+}
+
+// Compact plan of the experts that received tokens (decode path):
+//   plan[0] = n_active; for a < n_active: plan[1+3a] = expert,
+//   plan[2+3a] = first bucket row, plan[3+3a] = one past the last.
+inline size_t plan_ints(int max_active) { return 1 + 3 * (size_t)max_active; }
+
+// routing ------------------------------------------------------------------
+hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t *wr,
+                                float *logits, hipStream_t s);
+// selection; when `plan` is non-null (T*k <= kSmallSlots) it also buckets
+// the slots: sorted_token/sorted_slot/slot_pos/row_w [T*k], offsets [E+1]
+// (optional) and the compact plan.
+constexpr int kSmallSlots = 1024;
+hipError_t launch_select(int mode, int T, int E, int k, const float *logits,
+                         const int64_t *token_ids, int32_t *idx, float *w, int32_t *offsets,
+                         int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
+                         float *row_w, int32_t *plan, hipStream_t s);
+
+// dispatch -----------------------------------------------------------------
+size_t dispatch_ws_bytes(int T, int E, int k);
+hipError_t launch_dispatch(int T, int E, int k, const int32_t *idx, int32_t *offsets,
+                           int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
+                           void *ws, hipStream_t s);
+// compact plan from expert offsets (E+1 ints)
+hipError_t launch_plan_from_offsets(int E, const int32_t *offsets, int32_t *plan, hipStream_t s);
+
+// dequantize ---------------------------------------------------------------
+hipError_t launch_dequant(const WView &w, int expert, int64_t w0, int64_t count, float *out,
+                          hipStream_t s);
+
+// decode GEMVs ---------------------------------------------------------------
+// a[r][i] = silu(gate_e[i] . x[tok[r]]) * (up_e[i] . x[tok[r]]) for the plan's rows
+hipError_t launch_gateup_gemv(const WView &gate, const WView &up, int H, int I,
+                              const uint16_t *x, const int32_t *plan, int max_active,
+                              const int32_t *row_token, float *a, hipStream_t s);
+// y[r][n] = down_e[n] . a[r] for the plan's rows
+hipError_t launch_down_gemv(const WView &down, int H, int I, const float *a,
+                            const int32_t *plan, int max_active, float *y, hipStream_t s);
+// out[t][n] = shared_y[t][n] + sum over the plan's rows r of token t: row_w[r] * down_e[n].a[r]
+hipError_t launch_down_combine(const WView &down, int H, int I, int T, const float *a,
+                               const int32_t *plan, int max_active, const int32_t *row_token,
+                               const float *row_w, const float *shared_y, float *out,
+                               uint16_t *out_bf16, hipStream_t s);
+
+// combine -----------------------------------------------------------------
+hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
+                          const float *w, const float *shared_y, float *out, uint16_t *out_bf16,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,403 @@
+// route.hip -- router logits, expert selection and slot bucketing.
+//
+// Router (kept at full precision on the ds4 pages: dibi8.com guide "Key
+// innovations" item 1, hysenlabs.com "Model support and quantization"):
+//   logits[t][e] = sum_h x[t][h] * Wr[e][h]
+// Each bf16 x bf16 product is exact in fp64 and, for activations and router
+// weights of ordinary range, so is every partial sum, so the fp64 result does
+// not depend on the summation order; it is rounded once to fp32.  This makes
+// the logits -- and therefore the selected experts -- reproducible bit for bit.
+//
+// Selection: softmax top-k (ties to the lower expert index) or SplitMix64 hash
+// routing (grapeot.me ds4 post: V4 Flash uses hash MoE routing); weights are
+// the softmax of the selected logits.
+//
+// Bucketing: a counting sort of the T*k slots by expert, stable in slot order.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ----------------------------------------------------------------------------
+// router logits
+// ----------------------------------------------------------------------------
+
+__device__ __forceinline__ double dot8_bf16_f64(uint4 a, uint4 b) {
+  double s = (double)bf16_lo(a.x) * (double)bf16_lo(b.x);
+  s = fma((double)bf16_hi(a.x), (double)bf16_hi(b.x), s);
+  s = fma((double)bf16_lo(a.y), (double)bf16_lo(b.y), s);
+  s = fma((double)bf16_hi(a.y), (double)bf16_hi(b.y), s);
+  s = fma((double)bf16_lo(a.z), (double)bf16_lo(b.z), s);
+  s = fma((double)bf16_hi(a.z), (double)bf16_hi(b.z), s);
+  s = fma((double)bf16_lo(a.w), (double)bf16_lo(b.w), s);
+  s = fma((double)bf16_hi(a.w), (double)bf16_hi(b.w), s);
+  return s;
+}
+
+// one wave per logit; lanes stride over h in 8-element chunks (H % 8 == 0)
+__global__ __launch_bounds__(256) void k_router_gemv(int T, int H, int E,
+                                                      const uint16_t *__restrict__ x,
+                                                      const uint16_t *__restrict__ wr,
+                                                      float *__restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  for (int o = blockIdx.x * 4 + (threadIdx.x >> 6); o < T * E; o += nw) {
+    const int t = o / E, e = o - t * E;
+    const uint16_t *xr = x + (size_t)t * H;
+    const uint16_t *wrow = wr + (size_t)e * H;
+    double acc = 0.0;
+    for (int h = lane * 8; h < H; h += 512)
+      acc += dot8_bf16_f64(*reinterpret_cast<const uint4 *>(xr + h),
+                           *reinterpret_cast<const uint4 *>(wrow + h));
+    acc = group_sum_f64<64>(acc);
+    if (lane == 0) logits[(size_t)t * E + e] = (float)acc;
+  }
+}
+
+// tiled fp64 GEMM for many tokens: 32 tokens x 64 experts per block, each
+// thread 2 x 4 outputs, K staged through LDS as fp64 in chunks of 16.
+__global__ __launch_bounds__(256) void k_router_gemm(int T, int H, int E,
+                                                      const uint16_t *__restrict__ x,
+                                                      const uint16_t *__restrict__ wr,
+                                                      float *__restrict__ logits) {
+  __shared__ double xs[16][33];
+  __shared__ double ws[16][65];
+  const int t0 = blockIdx.y * 32, e0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  double acc[2][4] = {};
+  for (int k0 = 0; k0 < H; k0 += 16) {
+    for (int i = tid; i < 32 * 16; i += 256) {
+      const int tt = i >> 4, kk = i & 15, t = t0 + tt;
+      xs[kk][tt] = (t < T && k0 + kk < H) ? (double)bf16_bits_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0;
+    }
+    for (int i = tid; i < 64 * 16; i += 256) {
+      const int ee = i >> 4, kk = i & 15, e = e0 + ee;
+      ws[kk][ee] = (e < E && k0 + kk < H) ? (double)bf16_bits_to_f32(wr[(size_t)e * H + k0 + kk]) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) {
+      const double a0 = xs[kk][ty * 2], a1 = xs[kk][ty * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const double b = ws[kk][tx * 4 + j];
+        acc[0][j] = fma(a0, b, acc[0][j]);
+        acc[1][j] = fma(a1, b, acc[1][j]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int t = t0 + ty * 2 + i, e = e0 + tx * 4 + j;
+      if (t < T && e < E) logits[(size_t)t * E + e] = (float)acc[i][j];
+    }
+}
+
+hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t *wr,
+                                float *logits, hipStream_t s) {
+  if (T <= 8) {
+    const int waves = T * E;
+    const int blocks = (waves + 3) / 4;
+    k_router_gemv<<<blocks, 256, 0, s>>>(T, H, E, x, wr, logits);
+  } else {
+    dim3 grid((E + 63) / 64, (T + 31) / 32);
+    k_router_gemm<<<grid, 256, 0, s>>>(T, H, E, x, wr, logits);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// selection
+// ----------------------------------------------------------------------------
+
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014, with Stafford's Mix13
+// finaliser): increment by the golden gamma, then mix.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// monotone map of a float to uint32 (NaN ranks as -inf); never 0
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (v != v) u = 0xFF800000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_val(float v) { return v != v ? -INFINITY : v; }
+
+constexpr int kMaxE = 1024;
+
+// One wave selects the k experts of one token.  Lane j < k returns choice j
+// in (*e_out, *w_out); other lanes return e = -1.
+__device__ void select_one(int mode, int E, int k, const float *__restrict__ l, int64_t tid,
+                           int lane, int *e_out, float *w_out) {
+  int my_e = -1;
+  float my_l = -INFINITY;
+  if (mode == MOE_ROUTE_HASH) {
+    const uint64_t z = splitmix64((uint64_t)tid);
+    if (lane < k) {
+      my_e = (int)((z + (uint64_t)lane) % (uint64_t)E);
+      my_l = l[my_e];
+    }
+  } else {
+    uint64_t keys[kMaxE / 64];
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; i++) {
+      const int e = lane + 64 * i;
+      keys[i] = e < E ? ((uint64_t)order_bits(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
+                      : 0ull;
+    }
+    for (int j = 0; j < k; j++) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxE / 64; i++) best = keys[i] > best ? keys[i] : best;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t other = __shfl_xor(best, o, 64);
+        best = other > best ? other : best;
+      }
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int i = 0; i < kMaxE / 64; i++)
+          if (i == (e >> 6)) keys[i] = 0;
+      }
+      if (lane == j) {
+        my_e = e;
+        my_l = l[e];
+      }
+    }
+  }
+  float m = lane < k ? order_val(my_l) : -INFINITY;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float ex = lane < k ? expf(order_val(my_l) - m) : 0.0f;
+  const float den = group_sum<64>(ex);
+  *e_out = my_e;
+  *w_out = ex / den;
+}
+
+// selection only: one wave per token
+__global__ __launch_bounds__(256) void k_select(int mode, int T, int E, int k,
+                                                 const float *__restrict__ logits,
+                                                 const int64_t *__restrict__ tids,
+                                                 int32_t *__restrict__ idx, float *__restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int e;
+  float wt;
+  select_one(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, lane, &e, &wt);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = e;
+    w[(size_t)t * k + lane] = wt;
+  }
+}
+
+// exclusive prefix sum over a 1024-thread block; returns the prefix of v,
+// *total gets the block sum.  tmp: 16 ints of shared memory.
+__device__ int block_excl_scan_1024(int v, int *tmp, int *total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += n;
+  }
+  if (lane == 63) tmp[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int c = tmp[i];
+    base += i < wv ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Selection of all T tokens plus bucketing of the n = T*k <= 1024 slots in
+// one 1024-thread block (the decode path: no second launch for dispatch).
+__global__ __launch_bounds__(1024) void k_select_plan(
+    int mode, int T, int E, int k, const float *__restrict__ logits,
+    const int64_t *__restrict__ tids, int32_t *__restrict__ idx, float *__restrict__ w,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_token,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos, float *__restrict__ row_w,
+    int32_t *__restrict__ plan) {
+  __shared__ int s_e[kSmallSlots];
+  __shared__ float s_w[kSmallSlots];
+  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_off[kMaxE];
+  __shared__ int s_tmp[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = T * k;
+  for (int t = wv; t < T; t += 16) {
+    int e;
+    float wt;
+    select_one(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, lane, &e, &wt);
+    if (lane < k) {
+      s_e[t * k + lane] = e;
+      s_w[t * k + lane] = wt;
+      idx[(size_t)t * k + lane] = e;
+      w[(size_t)t * k + lane] = wt;
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += 1024) s_cnt[e] = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < n) atomicAdd(&s_cnt[s_e[threadIdx.x]], 1);
+  __syncthreads();
+  const int e = threadIdx.x;
+  const int c = e < E ? s_cnt[e] : 0;
+  int total, n_active;
+  const int off = block_excl_scan_1024(c, s_tmp, &total);
+  const int apos = block_excl_scan_1024(c > 0 ? 1 : 0, s_tmp, &n_active);
+  if (e < E) {
+    s_off[e] = off;
+    if (offsets) offsets[e] = off;
+    if (c > 0 && plan) {
+      plan[1 + 3 * apos] = e;
+      plan[2 + 3 * apos] = off;
+      plan[3 + 3 * apos] = off + c;
+    }
+  }
+  if (e == 0) {
+    if (offsets) offsets[E] = n;
+    if (plan) plan[0] = n_active;
+  }
+  __syncthreads();
+  const int f = threadIdx.x;
+  if (f < n) {
+    const int ef = s_e[f];
+    int rank = 0;
+    for (int g = 0; g < f; g++) rank += s_e[g] == ef;
+    const int r = s_off[ef] + rank;
+    sorted_token[r] = f / k;
+    if (sorted_slot) sorted_slot[r] = f;
+    if (slot_pos) slot_pos[f] = r;
+    if (row_w) row_w[r] = s_w[f];
+  }
+}
+
+hipError_t launch_select(int mode, int T, int E, int k, const float *logits,
+                         const int64_t *token_ids, int32_t *idx, float *w, int32_t *offsets,
+                         int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
+                         float *row_w, int32_t *plan, hipStream_t s) {
+  if (sorted_token) {
+    k_select_plan<<<1, 1024, 0, s>>>(mode, T, E, k, logits, token_ids, idx, w, offsets,
+                                     sorted_token, sorted_slot, slot_pos, row_w, plan);
+  } else {
+    k_select<<<(T + 3) / 4, 256, 0, s>>>(mode, T, E, k, logits, token_ids, idx, w);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// dispatch for any number of slots: per-chunk counts -> scan -> stable scatter
+// ----------------------------------------------------------------------------
+
+constexpr int kChunk = 256;
+
+__global__ __launch_bounds__(kChunk) void k_chunk_counts(int n, int E, const int32_t *__restrict__ idx,
+                                                          int32_t *__restrict__ counts) {
+  __shared__ int s_cnt[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kChunk) s_cnt[e] = 0;
+  __syncthreads();
+  const int f = blockIdx.x * kChunk + threadIdx.x;
+  if (f < n) atomicAdd(&s_cnt[idx[f]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kChunk) counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// one 1024-thread block: thread e walks the chunks of expert e; then a scan
+// over experts turns per-chunk counts into global bucket starts
+__global__ __launch_bounds__(1024) void k_chunk_scan(int n, int nchunks, int E,
+                                                      int32_t *__restrict__ counts,
+                                                      int32_t *__restrict__ offsets) {
+  __shared__ int s_tmp[16];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int b = 0; b < nchunks; b++) {
+      const int c = counts[(size_t)b * E + e];
+      counts[(size_t)b * E + e] = tot;
+      tot += c;
+    }
+  int total;
+  const int off = block_excl_scan_1024(e < E ? tot : 0, s_tmp, &total);
+  if (e < E) {
+    offsets[e] = off;
+    for (int b = 0; b < nchunks; b++) counts[(size_t)b * E + e] += off;
+  }
+  if (e == 0) offsets[E] = n;
+}
+
+__global__ __launch_bounds__(kChunk) void k_chunk_scatter(int n, int E, int k,
+                                                           const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ base,
+                                                           int32_t *__restrict__ sorted_token,
+                                                           int32_t *__restrict__ sorted_slot,
+                                                           int32_t *__restrict__ slot_pos) {
+  __shared__ int s_e[kChunk];
+  const int f0 = blockIdx.x * kChunk;
+  const int f = f0 + threadIdx.x;
+  s_e[threadIdx.x] = f < n ? idx[f] : -1;
+  __syncthreads();
+  if (f < n) {
+    const int ef = s_e[threadIdx.x];
+    int rank = 0;
+    for (int g = 0; g < (int)threadIdx.x; g++) rank += s_e[g] == ef;
+    const int r = base[(size_t)blockIdx.x * E + ef] + rank;
+    sorted_token[r] = f / k;
+    if (sorted_slot) sorted_slot[r] = f;
+    if (slot_pos) slot_pos[f] = r;
+  }
+}
+
+size_t dispatch_ws_bytes(int T, int E, int k) {
+  const size_t n = (size_t)T * k;
+  const size_t nchunks = (n + kChunk - 1) / kChunk;
+  return nchunks * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch(int T, int E, int k, const int32_t *idx, int32_t *offsets,
+                           int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
+                           void *ws, hipStream_t s) {
+  const int n = T * k;
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  int32_t *counts = static_cast<int32_t *>(ws);
+  k_chunk_counts<<<nchunks, kChunk, 0, s>>>(n, E, idx, counts);
+  k_chunk_scan<<<1, 1024, 0, s>>>(n, nchunks, E, counts, offsets);
+  k_chunk_scatter<<<nchunks, kChunk, 0, s>>>(n, E, k, idx, counts, sorted_token, sorted_slot,
+                                             slot_pos);
+  return hipGetLastError();
+}
+
+// compact plan from offsets: one 1024-thread block (E <= 1024)
+__global__ __launch_bounds__(1024) void k_plan_from_offsets(int E, const int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ plan) {
+  __shared__ int s_tmp[16];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int n_active;
+  const int apos = block_excl_scan_1024(c > 0 ? 1 : 0, s_tmp, &n_active);
+  if (c > 0) {
+    plan[1 + 3 * apos] = e;
+    plan[2 + 3 * apos] = offsets[e];
+    plan[3 + 3 * apos] = offsets[e + 1];
+  }
+  if (e == 0) plan[0] = n_active;
+}
+
+hipError_t launch_plan_from_offsets(int E, const int32_t *offsets, int32_t *plan, hipStream_t s) {
+  k_plan_from_offsets<<<1, 1024, 0, s>>>(E, offsets, plan);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (so these run in a container with no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import routed_expert_ffn_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # an aligned, never dereferenced "device pointer"
+
+
+def _lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return moe.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_dequantize", "moe_last_error", "moe_abi_version", "moe_route_workspace",
+              "moe_dispatch_workspace", "moe_expert_ffn_workspace", "moe_forward_workspace"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert moe.abi_version() == 1
+
+
+def _w(fmt=moe.FMT_VQ2, E=8, N=2048, K=4096, data=FAKE, scales=FAKE, cb=FAKE):
+    return moe.Weights(fmt, E, N, K, data, scales, cb)
+
+
+def _err():
+    return moe.lib().moe_last_error().decode()
+
+
+def test_route_rejects_bad_arguments():
+    lib = _lib()
+    ok_args = dict(mode=0, T=4, H=256, E=8, k=2, x=FAKE, wr=FAKE, li=None, tid=None, idx=FAKE,
+                   w=FAKE, lo=FAKE, ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.moe_route(a["mode"], a["T"], a["H"], a["E"], a["k"], a["x"], a["wr"], a["li"],
+                             a["tid"], a["idx"], a["w"], a["lo"], a["ws"], a["wsb"], a["s"])
+
+    assert call(k=0) == moe.EINVAL and "k = 0" in _err()
+    assert call(k=9) == moe.EINVAL
+    assert call(k=17, E=32) == moe.EINVAL
+    assert call(E=0) == moe.EINVAL
+    assert call(E=2000) == moe.EINVAL
+    assert call(mode=7) == moe.EINVAL
+    assert call(T=-1) == moe.EINVAL
+    assert call(mode=1) == moe.EINVAL and "token_ids" in _err()
+    assert call(idx=None) == moe.EINVAL
+    assert call(x=None) == moe.EINVAL
+    assert call(H=100) == moe.EINVAL
+    assert call(x=FAKE + 2) == moe.EINVAL and "misaligned" in _err()
+    assert call(lo=None) == moe.ENOSPC
+    assert call(lo=None, ws=FAKE, wsb=lib.moe_route_workspace(4, 8) - 1) == moe.ENOSPC
+    assert call(T=0) == moe.OK  # no tokens: nothing to do, nothing enqueued
+
+
+def test_dispatch_rejects_bad_arguments():
+    lib = _lib()
+    f = lib.moe_dispatch
+    ws = lib.moe_dispatch_workspace(16, 8, 2)
+    assert ws > 0
+    assert f(16, 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == moe.EINVAL
+    assert f(16, 8, 2, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == moe.EINVAL
+    assert f(16, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == moe.ENOSPC
+    assert f(16, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.ENOSPC
+    assert f(0, 8, 2, None, None, None, None, None, None, 0, None) == moe.OK
+
+
+def test_expert_ffn_rejects_bad_arguments():
+    lib = _lib()
+    g, u, d = _w(), _w(), _w(moe.FMT_Q2K, 8, 4096, 2048, FAKE, None, None)
+    f = lib.moe_expert_ffn
+    ws = lib.moe_expert_ffn_workspace(1, 8, 8, 4096, 2048, moe.FMT_VQ2, moe.FMT_Q2K)
+
+    def call(g=g, u=u, d=d, H=4096, I=2048, off=FAKE, st=FAKE, n=8, ws_=ws):
+        return f(1, H, I, FAKE, C.byref(g), C.byref(u), C.byref(d), off, st, n, FAKE, FAKE, ws_,
+                 None)
+
+    assert call(H=2048) == moe.EINVAL and "shape" in _err()
+    assert call(u=_w(moe.FMT_MXFP4)) == moe.EUNSUPPORTED
+    assert call(u=_w(cb=FAKE + 1024)) == moe.EUNSUPPORTED and "codebook" in _err()
+    assert call(g=_w(scales=None), u=_w(scales=None)) == moe.EINVAL
+    assert call(g=_w(data=FAKE + 8), u=_w(data=FAKE + 8)) == moe.EINVAL
+    bad = _w(moe.FMT_VQ2, 8, 2048, 4000)
+    assert call(g=bad, u=bad, H=4000) == moe.EINVAL
+    odd = _w(moe.FMT_BF16, 8, 2048, 3072, FAKE, None, None)
+    dd = _w(moe.FMT_BF16, 8, 3072, 2048, FAKE, None, None)
+    assert call(g=odd, u=odd, d=dd, H=3072) == moe.EUNSUPPORTED
+    assert call(st=None) == moe.EINVAL
+    assert call(ws_=ws - 1) == moe.ENOSPC
+    assert call(off=None, n=5) == moe.EINVAL and "n_rows == T" in _err()
+    assert call(n=0) == moe.OK
+
+
+def test_combine_and_dequantize_reject_bad_arguments():
+    lib = _lib()
+    assert lib.moe_combine(4, 4096, 0, FAKE, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
+    assert lib.moe_combine(4, 4094, 8, FAKE, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
+    assert lib.moe_combine(4, 4096, 8, None, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
+    assert lib.moe_combine(0, 4096, 8, None, None, None, None, None, None, None) == moe.OK
+    w = _w(moe.FMT_Q2K, 2, 64, 256, FAKE, None, None)
+    dq = lib.moe_dequantize
+    assert dq(C.byref(w), 2, 0, 10, FAKE, None) == moe.EINVAL
+    assert dq(C.byref(w), 0, 64 * 256 - 5, 10, FAKE, None) == moe.EINVAL
+    assert dq(C.byref(w), 0, 0, 0, FAKE, None) == moe.OK
+    bad = _w(moe.FMT_Q2K, 1, 3, 100, FAKE, None, None)
+    assert dq(C.byref(bad), 0, 0, 10, FAKE, None) == moe.EINVAL
+    assert dq(C.byref(_w(fmt=9)), 0, 0, 10, FAKE, None) == moe.EUNSUPPORTED
+
+
+def test_forward_validation_and_workspace_sizes():
+    lib = _lib()
+    g, u = _w(E=256), _w(E=256)
+    d = _w(moe.FMT_Q2K, 256, 4096, 2048, FAKE, None, None)
+    L = moe.Layer(4096, 2048, 256, 8, 2048, 0, FAKE, g, u, d, FAKE, FAKE, FAKE)
+    ws1 = lib.moe_forward_workspace(C.byref(L), 1)
+    ws2048 = lib.moe_forward_workspace(C.byref(L), 2048)
+    assert 0 < ws1 < ws2048
+    f = lib.moe_forward
+    assert f(C.byref(L), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1 - 1, None) == moe.ENOSPC
+    assert f(C.byref(L), 0, None, None, None, None, None, None, None, None, 0, None) == moe.OK
+    Lh = moe.Layer(4096, 2048, 256, 8, 2048, 1, FAKE, g, u, d, FAKE, FAKE, FAKE)
+    assert f(C.byref(Lh), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1, None) == moe.EINVAL
+    Lk = moe.Layer(4096, 2048, 256, 0, 2048, 0, FAKE, g, u, d, FAKE, FAKE, FAKE)
+    assert f(C.byref(Lk), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1, None) == moe.EINVAL
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    _lib()
+    with pytest.raises(TypeError):
+        moe.dispatch(torch.zeros((4, 2), dtype=torch.int32), 8)

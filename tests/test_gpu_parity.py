@@ -1,0 +1,300 @@
+"""GPU parity: libmoe's HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Bit-exact: dequantized weights, router logits, selected experts, bucket
+arrays.  Floating point (routing weights, FFN rows, layer outputs): the
+normwise relative error max|y - y_ref| / max|y_ref| must stay within 2e-3;
+the weights within 1e-6 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_ffn_router_amd as moe
+import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="session")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def tiny():
+    return synth.gen_layer(synth.TINY, 0)
+
+
+@pytest.fixture(scope="session")
+def q2():
+    return synth.gen_layer(synth.Q2, 0)
+
+
+@pytest.fixture(scope="session")
+def mx():
+    return synth.gen_layer(synth.MX, 0)
+
+
+@pytest.fixture(scope="session")
+def dq2(q2, dev):
+    return moe.DeviceLayer.upload(q2, device=dev)
+
+
+@pytest.fixture(scope="session")
+def dmx(mx, dev):
+    return moe.DeviceLayer.upload(mx, device=dev)
+
+
+def t16(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+
+def tnp(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def normwise(y, ref):
+    ref = ref.astype(np.float64)
+    return np.abs(y.astype(np.float64) - ref).max() / max(np.abs(ref).max(), 1e-30)
+
+
+def bits_equal(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32),
+                          np.asarray(b, np.float32).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# dequantization: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,N,K", [
+    (synth.FMT_Q2K, 64, 1024), (synth.FMT_Q2K, 4, 128), (synth.FMT_Q2K, 7, 256),
+    (synth.FMT_VQ2, 64, 1024), (synth.FMT_VQ2, 3, 256),
+    (synth.FMT_MXFP4, 64, 1024), (synth.FMT_MXFP4, 5, 96),
+    (synth.FMT_BF16, 16, 512),
+])
+def test_dequant_stress_bit_exact(dev, fmt, N, K):
+    p = synth.gen_stress_proj(fmt, N, K, seed=N + K)
+    got = tnp(moe.dequantize(moe.DeviceProj.upload(p, dev)))
+    assert bits_equal(got, oracle.dequant(p))
+
+
+@pytest.mark.parametrize("which,expert,w0,count", [
+    ("gate", 0, 0, None), ("up", 255, 0, None), ("down", 7, 0, None),
+    ("down", 100, 12345, 70001), ("gate", 31, 4096 * 7 + 3, 9999),
+])
+def test_dequant_layer_bit_exact(dev, q2, mx, which, expert, w0, count):
+    for layer in (q2, mx):
+        p = getattr(layer, which)
+        dp = moe.DeviceProj.upload(p, dev)
+        got = tnp(moe.dequantize(dp, expert, w0, count))
+        assert bits_equal(got, oracle.dequant(p, expert, w0, count))
+
+
+# --------------------------------------------------------------------------
+# routing: logits and indices bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 4, 9, 37, 300, 2048])
+def test_router_softmax_topk(dev, q2, T):
+    x = synth.gen_x(4096, T, seed=100 + T)
+    idx, w, lo = moe.route(t16(x, dev), t16(q2.w_router, dev), 8)
+    ref_lo = oracle.router_logits(x, q2.w_router)
+    assert bits_equal(tnp(lo), ref_lo)
+    ref_idx, ref_w = oracle.select_topk(ref_lo, 8)
+    assert np.array_equal(tnp(idx), ref_idx)
+    np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6, atol=1e-7)
+
+
+def test_router_tiny(dev, tiny):
+    x = synth.gen_x(256, 4, seed=0)
+    idx, w, lo = moe.route(t16(x, dev), t16(tiny.w_router, dev), 2)
+    ref_idx, ref_w, ref_lo = oracle.LayerRef(tiny).route(x)
+    assert bits_equal(tnp(lo), ref_lo)
+    assert np.array_equal(tnp(idx), ref_idx)
+    np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6)
+
+
+@pytest.mark.parametrize("T", [1, 16, 4096])
+def test_router_hash(dev, q2, T):
+    x = synth.gen_x(4096, T, seed=7)
+    tids = synth.gen_token_ids(T, seed=T)
+    tids[0] = 0
+    if T > 1:
+        tids[1] = 129279
+    idx, w, lo = moe.route(t16(x, dev), t16(q2.w_router, dev), 8, mode=moe.ROUTE_HASH,
+                           token_ids=torch.from_numpy(tids).to(dev))
+    ref_idx, ref_w = oracle.select_hash(tids, tnp(lo), 8)
+    assert np.array_equal(tnp(idx), ref_idx)
+    assert list(ref_idx[0]) == list(range(175, 183))
+    np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6, atol=1e-7)
+
+
+def test_router_logits_in_zipf_and_ties(dev):
+    lg = synth.gen_zipf_logits(256, 16, 1.1, seed=0)
+    lg[3, :] = 0.5  # a token whose logits all tie: experts 0..7
+    lg[5, 10:20] = lg[5].max() + 1  # ten equal maxima
+    lt = torch.from_numpy(lg).to(dev)
+    idx, w, lo = moe.route(None, None, 8, logits_in=lt)
+    ref_idx, ref_w = oracle.select_topk(lg, 8)
+    assert np.array_equal(tnp(idx), ref_idx)
+    assert list(ref_idx[3]) == list(range(8)) and list(ref_idx[5]) == list(range(10, 18))
+    np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6)
+    assert bits_equal(tnp(lo), lg)
+
+
+# --------------------------------------------------------------------------
+# dispatch: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (16, 256, 8), (37, 8, 2), (2048, 256, 8),
+                                   (4096, 256, 8), (1000, 1024, 16), (300, 3, 3)])
+def test_dispatch_bit_exact(dev, T, E, k):
+    rng = np.random.default_rng(T * 31 + E)
+    p = (np.arange(1, E + 1) ** -1.1)
+    p /= p.sum()
+    idx = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(T)], np.int32)
+    got = [tnp(a) for a in moe.dispatch(torch.from_numpy(idx).to(dev), E)]
+    ref = oracle.dispatch(idx, E)
+    for g, r, name in zip(got, ref, ["offsets", "sorted_token", "sorted_slot", "slot_pos"]):
+        assert np.array_equal(g, r), name
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,H", [(1, 8, 4096), (16, 8, 4096), (300, 8, 256), (5, 2, 64)])
+def test_combine(dev, T, k, H):
+    rng = np.random.default_rng(T + k)
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    sp = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    out, ob = moe.combine(torch.from_numpy(y).to(dev), torch.from_numpy(sp).to(dev),
+                          torch.from_numpy(w).to(dev), torch.from_numpy(sh).to(dev),
+                          want_bf16=True)
+    ref = oracle.combine(y, sp, w.reshape(T, k), sh)
+    assert normwise(tnp(out), ref) < 1e-6
+    rb = torch.from_numpy(tnp(out)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(tnp(ob), rb)
+
+
+# --------------------------------------------------------------------------
+# expert FFN (bucketed and dense)
+# --------------------------------------------------------------------------
+
+def _bucketed_ffn_case(layer, dl, dev, T, seed):
+    R = oracle.LayerRef(layer)
+    x = synth.gen_x(layer.spec.H, T, seed=seed)
+    idx, w, _ = R.route(x)
+    off, st, ss, sp = oracle.dispatch(idx, layer.spec.E)
+    y = moe.expert_ffn(t16(x, dev), dl.gate, dl.up, dl.down, torch.from_numpy(off).to(dev),
+                       torch.from_numpy(st).to(dev))
+    return tnp(y), R.expert_ffn(x, off, st)
+
+
+def test_expert_ffn_tiny(dev, tiny):
+    dl = moe.DeviceLayer.upload(tiny, device=dev)
+    y, ref = _bucketed_ffn_case(tiny, dl, dev, 4, 0)
+    assert normwise(y, ref) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_expert_ffn_q2(dev, q2, dq2, T):
+    y, ref = _bucketed_ffn_case(q2, dq2, dev, T, 50 + T)
+    assert normwise(y, ref) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_expert_ffn_mxfp4(dev, mx, dmx, T):
+    y, ref = _bucketed_ffn_case(mx, dmx, dev, T, 60 + T)
+    assert normwise(y, ref) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 4, 7])
+def test_expert_ffn_dense_shared(dev, q2, dq2, T):
+    x = synth.gen_x(4096, T, seed=T)
+    sg = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_gate)
+    su = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_up)
+    sd = moe.DeviceProj(moe.FMT_BF16, 1, 4096, 2048, dq2.shared_down)
+    y = tnp(moe.expert_ffn(t16(x, dev), sg, su, sd))
+    ref = oracle.LayerRef(q2).shared_ffn(x)
+    assert normwise(y, ref) < TOL
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+def _forward_case(layer, dl, dev, T, seed, route=moe.ROUTE_SOFTMAX_TOPK, zipf=False):
+    x = synth.gen_x(layer.spec.H, T, seed=seed)
+    lg = synth.gen_zipf_logits(layer.spec.E, T, 1.1, seed=seed) if zipf else None
+    tids = synth.gen_token_ids(T, seed=seed) if route == moe.ROUTE_HASH else None
+    ref, ref_idx, ref_w = oracle.LayerRef(layer, route_mode=route).forward(x, lg, tids)
+    L = dl.with_route_mode(route)
+    out, idx, w = moe.forward(L, t16(x, dev), None if lg is None else torch.from_numpy(lg).to(dev),
+                              None if tids is None else torch.from_numpy(tids).to(dev))
+    out, idx, w = tnp(out), tnp(idx), tnp(w)
+    assert np.array_equal(idx, ref_idx)
+    np.testing.assert_allclose(w, ref_w, rtol=1e-6, atol=1e-7)
+    err = normwise(out, ref)
+    assert err < TOL, err
+    return out
+
+
+def test_forward_tiny(dev, tiny):
+    dl = moe.DeviceLayer.upload(tiny, device=dev)
+    for T in (1, 4, 13):
+        _forward_case(tiny, dl, dev, T, seed=T)
+
+
+def test_forward_decode_b1(dev, q2, dq2):
+    for seed in range(3):
+        _forward_case(q2, dq2, dev, 1, seed)
+
+
+def test_forward_decode_b16_zipf(dev, q2, dq2):
+    _forward_case(q2, dq2, dev, 16, 0, zipf=True)
+
+
+@pytest.mark.parametrize("T", [2, 64, 200])
+def test_forward_q2_batches(dev, q2, dq2, T):
+    _forward_case(q2, dq2, dev, T, 1000 + T)
+
+
+@pytest.mark.parametrize("route", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
+def test_forward_mxfp4_decode(dev, mx, dmx, route):
+    _forward_case(mx, dmx, dev, 1, 3, route=route)
+    _forward_case(mx, dmx, dev, 9, 4, route=route)
+
+
+def test_forward_deterministic(dev, q2, dq2):
+    x = t16(synth.gen_x(4096, 16, seed=5), dev)
+    a, _, _ = moe.forward(dq2, x)
+    b, _, _ = moe.forward(dq2, x)
+    assert np.array_equal(tnp(a).view(np.uint32), tnp(b).view(np.uint32))
+
+
+def test_forward_equals_composed_calls(dev, q2, dq2):
+    """moe_forward vs moe_route -> moe_dispatch -> moe_expert_ffn x2 -> moe_combine."""
+    T = 24
+    x = t16(synth.gen_x(4096, T, seed=8), dev)
+    out, idx, w = moe.forward(dq2, x)
+    idx2, w2, _ = moe.route(x, dq2.w_router, 8)
+    off, st, ss, sp = moe.dispatch(idx2, 256)
+    y = moe.expert_ffn(x, dq2.gate, dq2.up, dq2.down, off, st)
+    sg = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_gate)
+    su = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_up)
+    sd = moe.DeviceProj(moe.FMT_BF16, 1, 4096, 2048, dq2.shared_down)
+    sh = moe.expert_ffn(x, sg, su, sd)
+    out2, _ = moe.combine(y, sp, w2, sh)
+    assert np.array_equal(tnp(idx), tnp(idx2))
+    assert normwise(tnp(out2), tnp(out).astype(np.float64)) < 1e-5
