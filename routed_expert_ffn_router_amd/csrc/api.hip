@@ -10,6 +10,7 @@
 
 namespace moe {
 bool gemv_supported_k(int K);
+bool down_combine_supported(int I);
 }
 
 using namespace moe;
@@ -187,7 +188,7 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.slot_pos = c.take<int32_t>(n);
     b.row_w = c.take<float>(n);
     b.a = c.take<float>(n * I);
-    if (T > 1) b.y_rows = c.take<float>(n * H);
+    b.y_rows = c.take<float>(n * H);
   } else {
     b.offsets = c.take<int32_t>(E + 1);
     b.sorted_token = c.take<int32_t>(n);
@@ -387,7 +388,7 @@ int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logit
     const int max_active = std::min(E, n);
     MOE_TRY(hip_check(
         launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s), "gate/up"));
-    if (T == 1)
+    if (T == 1 && down_combine_supported(I))
       return hip_check(launch_down_combine(d, H, I, T, b.a, b.plan, max_active, b.sorted_token,
                                            b.row_w, b.shared_y, out_f32, out_bf16, s),
                        "down+combine");

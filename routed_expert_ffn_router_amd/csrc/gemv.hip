@@ -670,6 +670,11 @@ bool gemv_supported_k(int K) {
   return geometry(K, &spl, &lpr);
 }
 
+bool down_combine_supported(int I) {
+  int spl, lpr;
+  return geometry(I, &spl, &lpr) && lpr == 64;
+}
+
 hipError_t launch_gateup_gemv(const WView &gate, const WView &up, int H, int I,
                               const uint16_t *x, const int32_t *plan, int max_active,
                               const int32_t *row_token, float *a, hipStream_t s) {
