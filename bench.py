@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed-expert MoE FFN layer on one MI355X.
+
+Headline: decode tokens/s of a DeepSeek-V4-Flash-class MoE layer (hidden
+4096, 256 routed experts + 1 bf16 shared expert, intermediate 2048, top-8
+softmax routing; gate/up in the 2.06-bit VQ2 codebook format, down in Q2K),
+batch 1, with the achieved HBM bandwidth; prefill tokens/s at 2048 tokens is
+reported beside it.  Inputs are synthetic and seeded (synth/).
+
+A step is one moe_forward over one batch of tokens: route, dispatch, expert
+FFNs (dequant fused), shared expert, combine.  The weights are held in R
+replicas in distinct HBM so that consecutive steps never find them in the
+256 MB last-level cache; every step uses a new token batch.  Decode steps are
+replayed from HIP graphs of G consecutive steps (launch cost amortised).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s; prefill tokens/s @2048"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="decode_b1")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--graph-steps", type=int, default=64)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--marked-steps", type=int, default=40)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", default="prefill_2048",
+                    help="comma-separated extra workloads measured after the headline")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# algorithmic bytes / flops
+# --------------------------------------------------------------------------
+
+def kernel_bytes(name, L, T, U, n):
+    """Algorithmic HBM bytes of one launch of kernel `name` (weights read once,
+    activations read/written once).  U: experts that received tokens; n = T*k."""
+    H, I, E, Is = L.H, L.I, L.E, L.I_shared
+    gu = L.gate.nbytes_per_expert() + L.up.nbytes_per_expert()
+    dn = L.down.nbytes_per_expert()
+    cb = 1024 if L.gate.fmt == 2 else 0
+    table = {
+        "router": E * H * 2 + T * H * 2 + T * E * 4,
+        "shared_gateup": 2 * Is * H * 2 + T * H * 2 + T * Is * 4,
+        "shared_down": H * Is * 2 + T * Is * 4 + T * H * 4,
+        "select_plan": T * E * 4 + n * 16,
+        "select": T * E * 4 + n * 8,
+        "routed_gateup": U * gu + cb + T * H * 2 + n * I * 4,
+        "gateup_gemv": U * gu + cb + T * H * 2 + n * I * 4,
+        "down_combine": U * dn + n * I * 4 + T * H * 8,
+        "routed_down": U * dn + n * I * 4 + n * H * 4,
+        "down_gemv": U * dn + n * I * 4 + n * H * 4,
+        "combine": n * H * 4 + T * H * 8 + n * 8,
+        "dispatch": n * 4 * 5,
+        "plan": (E + 1) * 4,
+    }
+    return table.get(name, 0)
+
+
+def step_bytes(L, T, U):
+    """Weights streamed once per step + activations in and out."""
+    gu = L.gate.nbytes_per_expert() + L.up.nbytes_per_expert()
+    dn = L.down.nbytes_per_expert()
+    shared = 3 * L.I_shared * L.H * 2
+    router = L.E * L.H * 2
+    cb = 1024 if L.gate.fmt == 2 else 0
+    return U * (gu + dn) + shared + router + cb + T * L.H * 2 + T * L.H * 4
+
+
+def step_flops(L, T):
+    return 2 * T * (L.k * 3 * L.H * L.I + 3 * L.H * L.I_shared + L.E * L.H)
+
+
+# --------------------------------------------------------------------------
+# setup
+# --------------------------------------------------------------------------
+
+def setup(wname, replicas, seed, npool, dev):
+    import torch
+
+    import routed_expert_ffn_router_amd as moe
+    import synth
+
+    w = synth.WORKLOADS[wname]
+    host = synth.gen_layer(w.layer, seed)
+    base = moe.DeviceLayer.upload(host, route_mode=w.route, device=dev)
+    layers = [base] + [base.clone() for _ in range(replicas - 1)]
+    xs, lgs, tids = [], [], []
+    for i in range(npool):
+        x, lg, ti = synth.gen_step_inputs(w, seed, step=i)
+        xs.append(torch.from_numpy(x.view(np.int16)).to(dev))
+        lgs.append(None if lg is None else torch.from_numpy(lg).to(dev))
+        tids.append(None if ti is None else torch.from_numpy(ti).to(dev))
+    return w, host, layers, xs, lgs, tids
+
+
+def unique_experts(f, layers, xs, lgs, tids, n=8):
+    import torch
+
+    us = []
+    for i in range(min(n, len(xs))):
+        f(xs[i], lgs[i], tids[i], layer=layers[i % len(layers)])
+        torch.cuda.synchronize()
+        us.append(len(torch.unique(f.idx)))
+    return float(np.mean(us))
+
+
+def time_steps(f, layers, xs, lgs, tids, steps, warmup, graph_steps, use_graph):
+    """Seconds per step over exactly `steps` steps."""
+    import torch
+
+    R, P = len(layers), len(xs)
+
+    def run(i):
+        f(xs[i % P], lgs[i % P], tids[i % P], layer=layers[i % R])
+
+    if use_graph:
+        G = max(g for g in range(1, graph_steps + 1) if steps % g == 0)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(warmup):
+                run(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                run(i)
+        g.replay()
+        torch.cuda.synchronize()
+        # the graph's last step must equal the same step run eagerly
+        gout = f.out.clone()
+        run(G - 1)
+        torch.cuda.synchronize()
+        if not torch.equal(gout, f.out):
+            raise RuntimeError("graph replay differs from eager execution")
+        reps = steps // G
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / 1e3 / steps, G
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3 / steps, 1
+
+
+def kernel_times(f, layers, xs, lgs, tids, steps):
+    """Average duration (s) of each kernel of a step, from HIP events that
+    moe_forward_marked records between its kernels on the launch stream."""
+    import torch
+
+    R, P = len(layers), len(xs)
+    nmax = 16
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nmax)] for _ in range(steps)]
+    for row in evs:  # torch creates the HIP event on first record
+        for ev in row:
+            ev.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(60_000_000)  # keep the GPU busy while the host enqueues every step
+    names = None
+    for i in range(steps):
+        nm = f.marked(xs[i % P], evs[i], lgs[i % P], tids[i % P], layer=layers[i % R])
+        names = names or nm
+    torch.cuda.synchronize()
+    acc = {}
+    for i in range(steps):
+        for j in range(len(names) - 1):
+            acc.setdefault(names[j], []).append(evs[i][j].elapsed_time(evs[i][j + 1]) / 1e3)
+    return {k: float(np.mean(v[1:] if len(v) > 2 else v)) for k, v in acc.items()}
+
+
+def cpu_baseline(host, w, seed, budget_s):
+    import oracle
+    import synth
+
+    R = oracle.LayerRef(host, route_mode=w.route)
+    n, t_total = 0, 0.0
+    while n < 2 or (t_total < budget_s and n < 1000):
+        x, lg, ti = synth.gen_step_inputs(w, seed, step=10_000 + n)
+        t0 = time.perf_counter()
+        R.forward(x, lg, ti)
+        t_total += time.perf_counter() - t0
+        n += 1
+    return {"value": n * w.T / t_total, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{n} steps of {w.name} (T={w.T}) through the full oracle layer "
+                      f"(route, dequantize the selected experts, fp64 FFNs, combine); "
+                      f"{t_total:.1f} s"}
+
+
+def measure(wname, args, dev, headline):
+    import routed_expert_ffn_router_amd as moe
+
+    w, host, layers, xs, lgs, tids = setup(wname, args.replicas if headline else 2, 0,
+                                           64 if w_is_decode(wname) else 4, dev)
+    L = layers[0]
+    f = moe.Forward(L, w.T, dev)
+    U = unique_experts(f, layers, xs, lgs, tids)
+    decode = w_is_decode(wname)
+    steps = args.steps if headline else args.extra_steps
+    warm = args.warmup if headline else 1
+    sec, G = time_steps(f, layers, xs, lgs, tids, steps, warm, args.graph_steps,
+                        decode and not args.no_graph)
+    kt = kernel_times(f, layers, xs, lgs, tids, args.marked_steps if headline else 3)
+    res = {"workload": wname, "T": w.T, "sec_per_step": sec, "tokens_per_s": w.T / sec,
+           "unique_experts": U, "graph_steps": G,
+           "hbm_bytes_per_step": step_bytes(L, w.T, U),
+           "hbm_gbps": step_bytes(L, w.T, U) / sec / 1e9,
+           "tflops": step_flops(L, w.T) / sec / 1e12,
+           "kernels_us": {k: v * 1e6 for k, v in kt.items()}}
+    dom = max(kt, key=kt.get)
+    nb = kernel_bytes(dom, L, w.T, U, w.T * L.k)
+    res["dominant"] = {"kernel": dom, "us": kt[dom] * 1e6, "bytes": nb,
+                       "gbps": nb / kt[dom] / 1e9}
+    return res, host, w, L
+
+
+def w_is_decode(wname):
+    import synth
+    return synth.WORKLOADS[wname].T <= 64
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "libmoe runs on one GPU: the layer is not sharded here "
+                          "(see the sharding design note); run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    head, host, w, L = measure(args.workload, args, dev, True)
+    d = head["dominant"]
+    roof = {"bound": "hbm", "kernel": d["kernel"], "achieved": d["gbps"], "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": d["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+            "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]}
+    extras = {}
+    for name in [e for e in args.extras.split(",") if e and e != args.workload]:
+        torch.cuda.empty_cache()
+        r, _, _, _ = measure(name, args, dev, False)
+        extras[name] = r
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, w, 0, args.cpu_seconds)
+    fmt = {0: "bf16", 1: "q2k", 2: "vq2", 3: "mxfp4"}
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["sec_per_step"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "H": L.H, "I": L.I, "E": L.E, "k": L.k,
+                   "T": w.T, "I_shared": L.I_shared, "gate_up": fmt[L.gate.fmt],
+                   "down": fmt[L.down.fmt], "shared": "bf16", "replicas": args.replicas},
+        "hbm_gbps": head["hbm_gbps"],
+        "hbm_frac": head["hbm_gbps"] / HBM_PEAK_GBPS,
+        "hbm_bytes_per_step": head["hbm_bytes_per_step"],
+        "unique_experts": head["unique_experts"],
+        "kernels_us": head["kernels_us"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,6 +172,21 @@ int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *l
                 int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                 void *stream);
 
+/* moe_forward_marked: moe_forward for measurement tools.  Before each
+ * kernel it enqueues, and once after the last, it records the caller's event
+ * marks[i].event (a hipEvent_t passed as void*) on `stream` and sets
+ * marks[i].name to a static string naming the kernel that follows ("end"
+ * for the last mark).  At most max_marks marks are recorded; *n_marks gets
+ * the number recorded.  Results are identical to moe_forward. */
+typedef struct {
+  void *event;
+  const char *name;
+} moe_mark;
+int moe_forward_marked(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,
+                       const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                       int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                       moe_mark *marks, int max_marks, int *n_marks, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* moe_dequantize: weights [w0, w0+count) of expert `expert`'s row-major
  * flattened matrix, decoded to fp32 with the same device decoders the FFN

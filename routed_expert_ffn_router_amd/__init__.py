@@ -40,6 +40,10 @@ class Layer(C.Structure):
                 ("shared_down", C.c_void_p)]
 
 
+class Mark(C.Structure):
+    _fields_ = [("event", C.c_void_p), ("name", C.c_char_p)]
+
+
 _lib = None
 
 
@@ -75,6 +79,8 @@ def lib():
         L.moe_forward_workspace.argtypes = [C.POINTER(Layer), i32]
         L.moe_forward.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dequantize.argtypes = [C.POINTER(Weights), i32, i64, i64, vp, vp]
+        L.moe_forward_marked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         C.POINTER(Mark), i32, C.POINTER(i32), vp]
         _lib = L
     return _lib
 
@@ -290,6 +296,19 @@ class Forward:
                                  _ptr(self.out), _ptr(self.out_bf16), _ptr(self.idx), _ptr(self.w),
                                  _ptr(self.ws), self.ws.numel(), _stream()))
         return self.out
+
+
+    def marked(self, x, events, logits_in=None, token_ids=None, layer=None):
+        """moe_forward_marked: records torch.cuda.Event objects between kernels;
+        returns the kernel names (one per interval)."""
+        L = self.layer if layer is None else layer
+        marks = (Mark * len(events))(*[Mark(ev.cuda_event, None) for ev in events])
+        n = C.c_int(0)
+        _check(lib().moe_forward_marked(C.byref(L.c), self.T, _ptr(x), _ptr(logits_in),
+                                        _ptr(token_ids), _ptr(self.out), _ptr(self.out_bf16),
+                                        _ptr(self.idx), _ptr(self.w), _ptr(self.ws), self.ws.numel(),
+                                        marks, len(events), C.byref(n), _stream()))
+        return [marks[i].name.decode() for i in range(n.value)]
 
 
 def forward(layer, x, logits_in=None, token_ids=None):

@@ -10,7 +10,6 @@
 
 namespace moe {
 bool gemv_supported_k(int K);
-bool down_combine_supported(int I);
 }
 
 using namespace moe;
@@ -114,6 +113,27 @@ int check_ffn_weights(int E, int H, int I, const moe_weights *gate, const moe_we
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
+// Optional event marks between kernels (moe_forward_marked).
+struct Marker {
+  moe_mark *m = nullptr;
+  int max = 0, n = 0;
+  hipStream_t s = nullptr;
+  hipError_t err = hipSuccess;
+  void operator()(const char *name) {
+    if (m && n < max) {
+      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(m[n].event), s);
+      if (e != hipSuccess) {
+        if (err == hipSuccess) err = e;
+        (void)hipGetLastError();  // do not leave it for the next launch check
+      }
+      m[n].name = name;
+      n++;
+    }
+  }
+};
+
+void mark_cb(void *ctx, const char *name) { (*static_cast<Marker *>(ctx))(name); }
+
 WView bf16_view(const uint16_t *p, int N, int K) {
   return WView{MOE_FMT_BF16, 1, N, K, reinterpret_cast<const uint8_t *>(p), nullptr, nullptr};
 }
@@ -136,16 +156,23 @@ FfnBufs carve_ffn(Carver &c, int n_rows, int E, int I, bool dense) {
 
 int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView &u,
             const WView &d, const int32_t *offsets, const int32_t *sorted_token, int n_rows,
-            float *y, const FfnBufs &b, hipStream_t s) {
+            float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
+  Marker none;
+  Marker &m = mk ? *mk : none;
   if (!offsets) {
+    m("gateup_gemv");
     MOE_TRY(hip_check(launch_gateup_gemv(g, u, H, I, x, nullptr, T, nullptr, b.a, s), "gate/up"));
+    m("down_gemv");
     return hip_check(launch_down_gemv(d, H, I, b.a, nullptr, T, y, s), "down");
   }
   const int E = g.E;
   const int max_active = std::min(E, n_rows);
+  m("plan");
   MOE_TRY(hip_check(launch_plan_from_offsets(E, offsets, b.plan, s), "plan"));
+  m("gateup_gemv");
   MOE_TRY(hip_check(launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, sorted_token, b.a, s),
                     "gate/up"));
+  m("down_gemv");
   return hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, y, s), "down");
 }
 
@@ -154,6 +181,7 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
 // ---------------------------------------------------------------------------
 
 struct FwdBufs {
+  bool decode1;
   float *logits;
   int32_t *idx;
   float *w;
@@ -169,6 +197,12 @@ struct FwdBufs {
 
 bool fwd_small(const moe_layer *L, int T) { return (long long)T * L->k <= kSmallSlots; }
 
+bool has_shared(const moe_layer *L) { return L->I_shared > 0 && L->shared_gate; }
+
+bool fwd_decode1(const moe_layer *L, int T) {
+  return T == 1 && decode1_supported(L->H, L->I, has_shared(L) ? L->I_shared : 0, L->k);
+}
+
 FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool have_idx,
                   bool have_w) {
   FwdBufs b{};
@@ -182,7 +216,10 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.a_sh = c.take<float>((size_t)T * L->I_shared);
     b.shared_y = c.take<float>((size_t)T * H);
   }
-  if (fwd_small(L, T)) {
+  if (fwd_decode1(L, T)) {
+    b.decode1 = true;
+    b.a = c.take<float>(n * I);
+  } else if (fwd_small(L, T)) {
     b.plan = c.take<int32_t>(plan_ints(std::min<size_t>(E, n)));
     b.sorted_token = c.take<int32_t>(n);
     b.slot_pos = c.take<int32_t>(n);
@@ -343,10 +380,10 @@ size_t moe_forward_workspace(const moe_layer *L, int T) {
   return c.size();
 }
 
-int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
-                const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
-                int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                void *stream) {
+static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
+                        const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                        int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                        void *stream, Marker &mk) {
   MOE_TRY(check_layer(L));
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (T == 0) return MOE_OK;
@@ -360,13 +397,37 @@ int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logit
     return fail(MOE_ENOSPC, "forward workspace: %zu bytes < %zu", ws_bytes, need);
 
   hipStream_t s = as_stream(stream);
+  mk.s = s;
   const int E = L->E, k = L->k, H = L->H, I = L->I, n = T * k;
   Carver c(ws);
   FwdBufs b = carve_fwd(c, L, T, false, false, false);
   int32_t *idx = topk_idx_out ? topk_idx_out : b.idx;
   float *w = topk_w_out ? topk_w_out : b.w;
+  if (b.decode1) {
+    DecodeArgs a{};
+    a.H = H, a.I = I, a.E = E, a.k = k, a.mode = L->route_mode;
+    a.Is = has_shared(L) ? L->I_shared : 0;
+    a.x = x, a.w_router = L->w_router, a.logits_in = logits_in, a.tid = token_ids;
+    a.gate = view_of(L->gate), a.up = view_of(L->up), a.down = view_of(L->down);
+    if (a.Is) {
+      a.sg = bf16_view(L->shared_gate, a.Is, H);
+      a.su = bf16_view(L->shared_up, a.Is, H);
+      a.sd = bf16_view(L->shared_down, H, a.Is);
+    }
+    a.logits = b.logits, a.a_sh = b.a_sh, a.shared_y = b.shared_y, a.a = b.a;
+    // the split forms reuse the fp32 buffers: two uint16 halves per float
+    a.a_sh_hi = reinterpret_cast<uint16_t *>(b.a_sh);
+    a.a_sh_lo = a.Is ? a.a_sh_hi + a.Is : nullptr;
+    a.a_hi = reinterpret_cast<uint16_t *>(b.a);
+    a.a_lo = a.a_hi + (size_t)k * I;
+    a.topk_idx = idx, a.topk_w = w, a.out = out_f32, a.out_bf16 = out_bf16;
+    const int rc = hip_check(launch_decode1(a, s, mark_cb, &mk), "decode");
+    mk("end");
+    return rc;
+  }
   const float *logits = logits_in;
   if (!logits) {
+    mk("router");
     MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
     logits = b.logits;
   }
@@ -375,39 +436,76 @@ int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logit
     const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
+    mk("shared_gateup");
     MOE_TRY(hip_check(launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, s),
                       "shared gate/up"));
+    mk("shared_down");
     MOE_TRY(hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, s),
                       "shared down"));
   }
   const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
+  int rc;
   if (fwd_small(L, T)) {
+    mk("select_plan");
     MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
                                     b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
                       "select"));
     const int max_active = std::min(E, n);
+    mk("routed_gateup");
     MOE_TRY(hip_check(
         launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s), "gate/up"));
-    if (T == 1 && down_combine_supported(I))
-      return hip_check(launch_down_combine(d, H, I, T, b.a, b.plan, max_active, b.sorted_token,
-                                           b.row_w, b.shared_y, out_f32, out_bf16, s),
-                       "down+combine");
+    mk("routed_down");
     MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
-    return hip_check(
+    mk("combine");
+    rc = hip_check(
         launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
         "combine");
+    mk("end");
+    return rc;
   }
+  mk("select");
   MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
                                   nullptr, nullptr, nullptr, nullptr, nullptr, s),
                     "select"));
+  mk("dispatch");
   MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
                                     b.slot_pos, b.dispatch_ws, s),
                     "dispatch"));
-  MOE_TRY(run_ffn(T, H, I, x, g, u, d, b.offsets, b.sorted_token, n, b.y_rows, b.ffn, s));
-  return hip_check(
+  MOE_TRY(run_ffn(T, H, I, x, g, u, d, b.offsets, b.sorted_token, n, b.y_rows, b.ffn, s, &mk));
+  mk("combine");
+  rc = hip_check(
       launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
       "combine");
+  mk("end");
+  return rc;
 }
+
+int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
+                const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                void *stream) {
+  Marker none;
+  return forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out, topk_w_out,
+                      ws, ws_bytes, stream, none);
+}
+
+int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
+                       const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                       int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                       moe_mark *marks, int max_marks, int *n_marks, void *stream) {
+  if (max_marks < 0 || (max_marks > 0 && !marks)) return fail(MOE_EINVAL, "bad marks");
+  for (int i = 0; i < max_marks; i++)
+    if (!marks[i].event) return fail(MOE_EINVAL, "mark %d has no event", i);
+  Marker mk;
+  mk.m = marks;
+  mk.max = max_marks;
+  const int rc = forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out,
+                              topk_w_out, ws, ws_bytes, stream, mk);
+  if (n_marks) *n_marks = mk.n;
+  if (rc == MOE_OK && mk.err != hipSuccess) return hip_check(mk.err, "event record");
+  return rc;
+}
+
 
 int moe_dequantize(const moe_weights *w, int expert, int64_t w0, int64_t count, float *out,
                    void *stream) {

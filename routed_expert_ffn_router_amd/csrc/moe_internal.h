@@ -78,11 +78,33 @@ hipError_t launch_gateup_gemv(const WView &gate, const WView &up, int H, int I,
 // y[r][n] = down_e[n] . a[r] for the plan's rows
 hipError_t launch_down_gemv(const WView &down, int H, int I, const float *a,
                             const int32_t *plan, int max_active, float *y, hipStream_t s);
-// out[t][n] = shared_y[t][n] + sum over the plan's rows r of token t: row_w[r] * down_e[n].a[r]
-hipError_t launch_down_combine(const WView &down, int H, int I, int T, const float *a,
-                               const int32_t *plan, int max_active, const int32_t *row_token,
-                               const float *row_w, const float *shared_y, float *out,
-                               uint16_t *out_bf16, hipStream_t s);
+
+// fused batch-1 decode (decode.hip) ------------------------------------------
+struct DecodeArgs {
+  int H, I, E, k, Is, mode;
+  const uint16_t *x;         // [H] bf16
+  const uint16_t *w_router;  // [E][H] bf16
+  const float *logits_in;    // optional [E]
+  const int64_t *tid;        // [1], hash routing
+  WView gate, up, down;      // routed experts
+  WView sg, su, sd;          // shared expert (bf16), when Is > 0
+  float *logits;             // [E]
+  float *a_sh;               // [Is] (also holds a_sh_hi / a_sh_lo)
+  uint16_t *a_sh_hi, *a_sh_lo;  // [Is] bf16 split of the shared SwiGLU output
+  float *shared_y;           // [H]
+  float *a;                  // [k][I] (also holds a_hi / a_lo)
+  uint16_t *a_hi, *a_lo;     // [k][I] bf16 split of the routed SwiGLU output
+  int a_mode;                // how a is stored (set by launch_decode1)
+  int32_t *topk_idx;         // [k]
+  float *topk_w;             // [k]
+  float *out;                // [H]
+  uint16_t *out_bf16;        // optional [H]
+  int nb_router, nb_shared_gu, nb_routed, nb_shared_down, tiles_per_expert;
+};
+
+bool decode1_supported(int H, int I, int Is, int k);
+hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, const char *),
+                          void *mark_ctx);
 
 // combine -----------------------------------------------------------------
 hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,

@@ -13,8 +13,7 @@
 // the softmax of the selected logits.
 //
 // Bucketing: a counting sort of the T*k slots by expert, stable in slot order.
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "select.h"
 
 namespace moe {
 
@@ -113,75 +112,6 @@ hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const ui
 // selection
 // ----------------------------------------------------------------------------
 
-// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014, with Stafford's Mix13
-// finaliser): increment by the golden gamma, then mix.
-__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
-  uint64_t z = x + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-// monotone map of a float to uint32 (NaN ranks as -inf); never 0
-__device__ __forceinline__ uint32_t order_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (v != v) u = 0xFF800000u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float order_val(float v) { return v != v ? -INFINITY : v; }
-
-constexpr int kMaxE = 1024;
-
-// One wave selects the k experts of one token.  Lane j < k returns choice j
-// in (*e_out, *w_out); other lanes return e = -1.
-__device__ void select_one(int mode, int E, int k, const float *__restrict__ l, int64_t tid,
-                           int lane, int *e_out, float *w_out) {
-  int my_e = -1;
-  float my_l = -INFINITY;
-  if (mode == MOE_ROUTE_HASH) {
-    const uint64_t z = splitmix64((uint64_t)tid);
-    if (lane < k) {
-      my_e = (int)((z + (uint64_t)lane) % (uint64_t)E);
-      my_l = l[my_e];
-    }
-  } else {
-    uint64_t keys[kMaxE / 64];
-#pragma unroll
-    for (int i = 0; i < kMaxE / 64; i++) {
-      const int e = lane + 64 * i;
-      keys[i] = e < E ? ((uint64_t)order_bits(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
-                      : 0ull;
-    }
-    for (int j = 0; j < k; j++) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; i++) best = keys[i] > best ? keys[i] : best;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t other = __shfl_xor(best, o, 64);
-        best = other > best ? other : best;
-      }
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      if ((e & 63) == lane) {
-#pragma unroll
-        for (int i = 0; i < kMaxE / 64; i++)
-          if (i == (e >> 6)) keys[i] = 0;
-      }
-      if (lane == j) {
-        my_e = e;
-        my_l = l[e];
-      }
-    }
-  }
-  float m = lane < k ? order_val(my_l) : -INFINITY;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  const float ex = lane < k ? expf(order_val(my_l) - m) : 0.0f;
-  const float den = group_sum<64>(ex);
-  *e_out = my_e;
-  *w_out = ex / den;
-}
-
 // selection only: one wave per token
 __global__ __launch_bounds__(256) void k_select(int mode, int T, int E, int k,
                                                  const float *__restrict__ logits,
@@ -192,7 +122,7 @@ __global__ __launch_bounds__(256) void k_select(int mode, int T, int E, int k,
   if (t >= T) return;
   int e;
   float wt;
-  select_one(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, lane, &e, &wt);
+  select_wave(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, &e, &wt);
   if (lane < k) {
     idx[(size_t)t * k + lane] = e;
     w[(size_t)t * k + lane] = wt;
@@ -241,7 +171,7 @@ __global__ __launch_bounds__(1024) void k_select_plan(
   for (int t = wv; t < T; t += 16) {
     int e;
     float wt;
-    select_one(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, lane, &e, &wt);
+    select_wave(mode, E, k, logits + (size_t)t * E, tids ? tids[t] : 0, &e, &wt);
     if (lane < k) {
       s_e[t * k + lane] = e;
       s_w[t * k + lane] = wt;
