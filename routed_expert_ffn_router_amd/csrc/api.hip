@@ -144,14 +144,28 @@ WView bf16_view(const uint16_t *p, int N, int K) {
 
 struct FfnBufs {
   int32_t *plan;
-  float *a;
+  float *a;        // fp32 SwiGLU output of the GEMV path; fp16 on the GEMM path
+  int32_t *tiles;  // GEMM tile list
 };
 
 FfnBufs carve_ffn(Carver &c, int n_rows, int E, int I, bool dense) {
   FfnBufs b;
   b.plan = dense ? nullptr : c.take<int32_t>(plan_ints(std::min(E, std::max(n_rows, 1))));
   b.a = c.take<float>((size_t)std::max(n_rows, 1) * I);
+  b.tiles = c.take<int32_t>(gemm_tile_ints(std::max(n_rows, 1), dense ? 0 : E));
   return b;
+}
+
+// 32-bit buffer offsets of the GEMM kernels: every operand below 2 GiB
+bool gemm_fits(int T, int H, int I, int n_rows) {
+  const size_t lim = (size_t)1 << 31;
+  return (size_t)T * H * 2 < lim && (size_t)n_rows * I * 2 < lim;
+}
+
+// the matrix cores pay once the buckets hold several rows each
+bool use_gemm(int T, int H, int I, int E, int n_rows, bool dense) {
+  if (!gemm_supported(H, I) || !gemm_fits(T, H, I, n_rows)) return false;
+  return dense ? n_rows >= 32 : (long long)n_rows >= 4LL * E;
 }
 
 int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView &u,
@@ -159,6 +173,10 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
             float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
   Marker none;
   Marker &m = mk ? *mk : none;
+  if (use_gemm(T, H, I, g.E, n_rows, !offsets))
+    return hip_check(launch_gemm_ffn(g, u, d, H, I, x, offsets, sorted_token, n_rows, b.tiles,
+                                     reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m),
+                     "gemm ffn");
   if (!offsets) {
     m("gateup_gemv");
     MOE_TRY(hip_check(launch_gateup_gemv(g, u, H, I, x, nullptr, T, nullptr, b.a, s), "gate/up"));
@@ -186,6 +204,7 @@ struct FwdBufs {
   int32_t *idx;
   float *w;
   float *a_sh, *shared_y;
+  int32_t *tiles_sh;
   // small path
   int32_t *plan, *sorted_token, *slot_pos;
   float *row_w, *a, *y_rows;
@@ -215,6 +234,7 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
   if (shared) {
     b.a_sh = c.take<float>((size_t)T * L->I_shared);
     b.shared_y = c.take<float>((size_t)T * H);
+    b.tiles_sh = c.take<int32_t>(gemm_tile_ints(T, 0));
   }
   if (fwd_decode1(L, T)) {
     b.decode1 = true;
@@ -436,12 +456,21 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
-    mk("shared_gateup");
-    MOE_TRY(hip_check(launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, s),
-                      "shared gate/up"));
-    mk("shared_down");
-    MOE_TRY(hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, s),
-                      "shared down"));
+    if (use_gemm(T, H, L->I_shared, 1, T, true)) {
+      mk("shared_gemm");
+      MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, x, nullptr, nullptr, T,
+                                        b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh),
+                                        b.shared_y, s, nullptr, nullptr),
+                        "shared gemm"));
+    } else {
+      mk("shared_gateup");
+      MOE_TRY(hip_check(
+          launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, s),
+          "shared gate/up"));
+      mk("shared_down");
+      MOE_TRY(hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, s),
+                        "shared down"));
+    }
   }
   const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
   int rc;

@@ -298,3 +298,109 @@ def test_forward_equals_composed_calls(dev, q2, dq2):
     out2, _ = moe.combine(y, sp, w2, sh)
     assert np.array_equal(tnp(idx), tnp(idx2))
     assert normwise(tnp(out2), tnp(out).astype(np.float64)) < 1e-5
+
+
+# --------------------------------------------------------------------------
+# prefill: the grouped-GEMM path (buckets of several rows per expert).
+# The oracle runs on sampled rows/tokens: a row of the expert FFN depends only
+# on its token and expert, a token's output only on its own input.
+# --------------------------------------------------------------------------
+
+def _sub_buckets(off, st, rows):
+    """The bucket arrays restricted to `rows` (bucket positions), in bucket order."""
+    rows = np.unique(np.asarray(rows))
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    cnt = np.bincount(e_of, minlength=len(off) - 1)
+    sub_off = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    return rows, sub_off, st[rows].astype(np.int32)
+
+
+def _gemm_rows_case(layer, dl, dev, x, off, st, n_sample, seed):
+    """expert_ffn over (off, st) on the GPU; sampled rows against the oracle."""
+    n = int(off[-1])
+    y = tnp(moe.expert_ffn(t16(x, dev), dl.gate, dl.up, dl.down, torch.from_numpy(off).to(dev),
+                           torch.from_numpy(st).to(dev)))
+    assert y.shape == (n, layer.spec.H) and np.isfinite(y).all()
+    rng = np.random.default_rng(seed)
+    # both ends of every tile boundary region, plus random rows
+    ends = np.concatenate([off[:-1][np.diff(off) > 0], off[1:][np.diff(off) > 0] - 1])
+    rows = np.concatenate([rng.choice(ends, min(len(ends), n_sample // 2), replace=False),
+                           rng.choice(n, n_sample // 2, replace=False), [0, n - 1]])
+    rows, sub_off, sub_st = _sub_buckets(off, st, rows)
+    ref = oracle.LayerRef(layer).expert_ffn(x, sub_off, sub_st)
+    return normwise(y[rows], ref)
+
+
+@pytest.mark.parametrize("T", [128, 161])
+def test_expert_ffn_gemm_q2(dev, q2, dq2, T):
+    x = synth.gen_x(4096, T, seed=70 + T)
+    idx, _, _ = oracle.LayerRef(q2).route(x)
+    off, st, _, _ = oracle.dispatch(idx, 256)
+    assert _gemm_rows_case(q2, dq2, dev, x, off, st, 48, T) < TOL
+
+
+def test_expert_ffn_gemm_mxfp4(dev, mx, dmx):
+    T = 150
+    x = synth.gen_x(4096, T, seed=80)
+    idx, _, _ = oracle.LayerRef(mx).route(x)
+    off, st, _, _ = oracle.dispatch(idx, 256)
+    assert _gemm_rows_case(mx, dmx, dev, x, off, st, 48, 81) < TOL
+
+
+def test_expert_ffn_gemm_ragged_buckets(dev, q2, dq2):
+    """Hand-made bucket sizes around the 64-row tile: 0, 1, 63, 64, 65, 127, 128, 129, ..."""
+    sizes = np.array([0, 1, 63, 64, 65, 127, 128, 129, 2, 0, 31, 3] * 22)[:256]
+    assert sizes.sum() >= 4 * 256
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 97
+    st = np.random.default_rng(5).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=90)
+    assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 91) < TOL
+
+
+@pytest.mark.parametrize("T", [32, 97])
+def test_expert_ffn_dense_shared_gemm(dev, q2, dq2, T):
+    x = synth.gen_x(4096, T, seed=T)
+    sg = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_gate)
+    su = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_up)
+    sd = moe.DeviceProj(moe.FMT_BF16, 1, 4096, 2048, dq2.shared_down)
+    y = tnp(moe.expert_ffn(t16(x, dev), sg, su, sd))
+    ref = oracle.LayerRef(q2).shared_ffn(x)
+    assert normwise(y, ref) < TOL
+
+
+def _forward_sampled(layer, dl, dev, T, seed, n_sample, route=moe.ROUTE_SOFTMAX_TOPK,
+                     zipf=False):
+    """Full-size forward on the GPU; routing of every token bit-exact against the
+    oracle, outputs of sampled tokens within the tolerance."""
+    x = synth.gen_x(layer.spec.H, T, seed=seed)
+    lg = synth.gen_zipf_logits(layer.spec.E, T, 1.1, seed=seed) if zipf else None
+    tids = synth.gen_token_ids(T, seed=seed) if route == moe.ROUTE_HASH else None
+    L = dl.with_route_mode(route)
+    out, idx, w = moe.forward(L, t16(x, dev), None if lg is None else torch.from_numpy(lg).to(dev),
+                              None if tids is None else torch.from_numpy(tids).to(dev))
+    out, idx, w = tnp(out), tnp(idx), tnp(w)
+    assert np.isfinite(out).all()
+    R = oracle.LayerRef(layer, route_mode=route)
+    ridx, rw, _ = R.route(x, lg, tids)
+    assert np.array_equal(idx, ridx)
+    np.testing.assert_allclose(w, rw, rtol=1e-6, atol=1e-7)
+    rng = np.random.default_rng(seed + 1)
+    sel = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
+    ref, _, _ = R.forward(x[sel], None if lg is None else lg[sel],
+                          None if tids is None else tids[sel])
+    err = normwise(out[sel], ref)
+    assert err < TOL, err
+
+
+def test_forward_prefill_2048(dev, q2, dq2):
+    _forward_sampled(q2, dq2, dev, 2048, 2048, 8)
+
+
+def test_forward_q2_zipf_gemm(dev, q2, dq2):
+    _forward_sampled(q2, dq2, dev, 256, 77, 8, zipf=True)
+
+
+@pytest.mark.parametrize("route", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
+def test_forward_mxfp4_prefill_4096(dev, mx, dmx, route):
+    _forward_sampled(mx, dmx, dev, 4096, 4096 + route, 6, route=route)
