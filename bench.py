@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s; prefill tokens/s @2048"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -56,29 +57,41 @@ def _args():
 # algorithmic bytes / flops
 # --------------------------------------------------------------------------
 
-def kernel_bytes(name, L, T, U, n):
-    """Algorithmic HBM bytes of one launch of kernel `name` (weights read once,
-    activations read/written once).  U: experts that received tokens; n = T*k."""
+def kernel_cost(name, L, T, U, n):
+    """(algorithmic HBM bytes, algorithmic flops) of one launch of kernel `name`:
+    every weight byte the launch needs read once, activations read and written
+    once.  U: experts that received tokens; n = T*k bucket rows."""
     H, I, E, Is = L.H, L.I, L.E, L.I_shared
     gu = L.gate.nbytes_per_expert() + L.up.nbytes_per_expert()
     dn = L.down.nbytes_per_expert()
     cb = 1024 if L.gate.fmt == 2 else 0
+    xb = T * H * 2
     table = {
-        "router": E * H * 2 + T * H * 2 + T * E * 4,
-        "shared_gateup": 2 * Is * H * 2 + T * H * 2 + T * Is * 4,
-        "shared_down": H * Is * 2 + T * Is * 4 + T * H * 4,
-        "select_plan": T * E * 4 + n * 16,
-        "select": T * E * 4 + n * 8,
-        "routed_gateup": U * gu + cb + T * H * 2 + n * I * 4,
-        "gateup_gemv": U * gu + cb + T * H * 2 + n * I * 4,
-        "down_combine": U * dn + n * I * 4 + T * H * 8,
-        "routed_down": U * dn + n * I * 4 + n * H * 4,
-        "down_gemv": U * dn + n * I * 4 + n * H * 4,
-        "combine": n * H * 4 + T * H * 8 + n * 8,
-        "dispatch": n * 4 * 5,
-        "plan": (E + 1) * 4,
+        # fused batch-1 decode: (1) shared gate/up + router, (2) shared down +
+        # select + routed gate/up, (3) routed down + combine
+        "decode_p1": (2 * Is * H * 2 + E * H * 2 + xb + Is * 4 + E * 4,
+                      2 * T * (2 * Is * H + E * H)),
+        "decode_p2": (H * Is * 2 + U * gu + cb + xb + Is * 4 + E * 4 + T * H * 4 + n * I * 4 + n * 8,
+                      2 * T * H * Is + 4 * n * I * H),
+        "decode_p3": (U * dn + n * I * 4 + n * 8 + 2 * T * H * 4, 2 * n * H * I),
+        "router": (E * H * 2 + xb + T * E * 4, 2 * T * E * H),
+        "shared_gateup": (2 * Is * H * 2 + xb + T * Is * 4, 4 * T * Is * H),
+        "shared_down": (H * Is * 2 + T * Is * 4 + T * H * 4, 2 * T * H * Is),
+        "shared_gemm": (3 * Is * H * 2 + xb + 2 * T * Is * 2 + T * H * 4, 6 * T * H * Is),
+        "select_plan": (T * E * 4 + n * 16, 0),
+        "select": (T * E * 4 + n * 8, 0),
+        "dispatch": (n * 4 * 5, 0),
+        "plan": ((E + 1) * 4, 0),
+        "tile_list": ((E + 1) * 4, 0),
+        "routed_gateup": (U * gu + cb + xb + n * I * 4, 4 * n * I * H),
+        "gateup_gemv": (U * gu + cb + xb + n * I * 4, 4 * n * I * H),
+        "routed_down": (U * dn + n * I * 4 + n * H * 4, 2 * n * H * I),
+        "down_gemv": (U * dn + n * I * 4 + n * H * 4, 2 * n * H * I),
+        "gemm_gateup": (U * gu + cb + xb + n * I * 2, 4 * n * I * H),
+        "gemm_down": (U * dn + n * I * 2 + n * H * 4, 2 * n * H * I),
+        "combine": (n * H * 4 + 2 * T * H * 4 + n * 8, 2 * n * H),
     }
-    return table.get(name, 0)
+    return table.get(name, (0, 0))
 
 
 def step_bytes(L, T, U):
@@ -245,11 +258,28 @@ def measure(wname, args, dev, headline):
            "hbm_bytes_per_step": step_bytes(L, w.T, U),
            "hbm_gbps": step_bytes(L, w.T, U) / sec / 1e9,
            "tflops": step_flops(L, w.T) / sec / 1e12,
-           "kernels_us": {k: v * 1e6 for k, v in kt.items()}}
+           }
+    per = {}
+    for name, t in kt.items():
+        nb, nf = kernel_cost(name, L, w.T, U, w.T * L.k)
+        per[name] = {"us": t * 1e6, "bytes": nb, "flops": nf, "gbps": nb / t / 1e9,
+                     "tflops": nf / t / 1e12}
+    res["kernels"] = per
     dom = max(kt, key=kt.get)
-    nb = kernel_bytes(dom, L, w.T, U, w.T * L.k)
-    res["dominant"] = {"kernel": dom, "us": kt[dom] * 1e6, "bytes": nb,
-                       "gbps": nb / kt[dom] / 1e9}
+    d = per[dom]
+    # a launch whose flops per algorithmic byte exceed the chip's balance point
+    # (2.5 PFLOP/s over 8 TB/s) is priced against the matrix cores
+    mfma = d["flops"] > (MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)) * d["bytes"]
+    if mfma:
+        res["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"],
+                           "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": d["tflops"] / MFMA_PEAK_TFLOPS, "traffic": None,
+                           "flops_per_launch": d["flops"], "us_per_launch": d["us"]}
+    else:
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": d["gbps"],
+                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": d["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                           "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]}
     return res, host, w, L
 
 
@@ -269,10 +299,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     head, host, w, L = measure(args.workload, args, dev, True)
-    d = head["dominant"]
-    roof = {"bound": "hbm", "kernel": d["kernel"], "achieved": d["gbps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": d["gbps"] / HBM_PEAK_GBPS, "traffic": None,
-            "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]}
+    roof = head["roofline"]
     extras = {}
     for name in [e for e in args.extras.split(",") if e and e != args.workload]:
         torch.cuda.empty_cache()
@@ -302,7 +329,7 @@ def main():
         "hbm_frac": head["hbm_gbps"] / HBM_PEAK_GBPS,
         "hbm_bytes_per_step": head["hbm_bytes_per_step"],
         "unique_experts": head["unique_experts"],
-        "kernels_us": head["kernels_us"],
+        "kernels": head["kernels"],
         "roofline": roof,
         "cpu_baseline": cpu,
         "extras": extras,

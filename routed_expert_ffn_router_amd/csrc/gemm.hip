@@ -234,7 +234,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   __shared__ uint32_t s_a[2][kBM * kLdsW];
   __shared__ uint32_t s_b[2][kBN * kLdsW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 : 1];
-  const int ti = blockIdx.y;
+  // XCD-aware order: workgroups go round-robin to the 8 XCDs, so linear id b
+  // runs on XCD b % 8.  Give XCD x the tiles x, x + 8, ... and walk all column
+  // blocks of one tile back to back there, so its L2 fetches each A tile once.
+  // (grid.y is a multiple of 8.)
+  const uint32_t nbx = gridDim.x;
+  const uint32_t b = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t j = b >> 3;
+  const int ti = (int)((j / nbx) * 8 + (b & 7));
+  const int bx = (int)(j % nbx);
   if (ti >= p.tiles[0]) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   constexpr int kCols = MODE == kModeGateUp ? kBN / 2 : kBN;  // output columns per tile
-  const int n0 = blockIdx.x * kCols;
+  const int n0 = bx * kCols;
 
   if constexpr (FMT == MOE_FMT_VQ2) {  // codebook entries as exact operand pairs
     const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[tid];
@@ -388,7 +396,7 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
                            void (*mark)(void *, const char *), void *mark_ctx) {
   if (!gemm_supported(H, I) || n_rows < 1) return hipErrorInvalidValue;
   const int E = offsets ? gate.E : 0;
-  const int max_tiles = (n_rows + kBM - 1) / kBM + E;
+  const int max_tiles = ((n_rows + kBM - 1) / kBM + E + 7) / 8 * 8;
   if (mark) mark(mark_ctx, "tile_list");
   k_tile_list<<<1, 1024, 0, s>>>(E, n_rows, offsets, tiles);
   hipError_t err = hipGetLastError();

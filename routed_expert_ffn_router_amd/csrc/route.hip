@@ -95,12 +95,69 @@ __global__ __launch_bounds__(256) void k_router_gemm(int T, int H, int E,
     }
 }
 
+// fp64 matrix cores for many tokens.  v_mfma_f64_16x16x4f64 takes A[l%16][l/16]
+// and B[l/16][l%16] from lane l and leaves D[4r + l/16][l%16] in its result
+// register r.  Which h the MFMA's reduction slot of a lane stands for is free
+// (the fp64 sum does not depend on the order): lane group g = l/16 feeds
+// h = h0 + 8g + s at step s, so each lane reads 8 consecutive bf16 of its row.
+// Block: 4 waves = 32 tokens x 64 experts; a wave holds 16 tokens x 32 experts
+// as two MFMA tiles, each split over two accumulators (even and odd steps) so
+// four independent chains fill the pipe.  H % 32 == 0, E % 64 == 0.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_router_mfma(int T, int H, int E,
+                                                      const uint16_t *__restrict__ x,
+                                                      const uint16_t *__restrict__ wr,
+                                                      float *__restrict__ logits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.y * 32 + 16 * (wave & 1);
+  const int e0 = blockIdx.x * 64 + 32 * (wave >> 1);
+  const int ta = min(t0 + r, T - 1);  // rows past T repeat the last token and are not stored
+  const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)ta * H + 8 * g);
+  const uint4 *wb0 = reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + r) * H + 8 * g);
+  const uint4 *wb1 = reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + 16 + r) * H + 8 * g);
+  f64x4_t c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+  const int n = H / 32;
+  uint4 a = xa[0], b0 = wb0[0], b1 = wb1[0];
+  for (int i = 0; i < n; i++) {
+    uint4 an = a, b0n = b0, b1n = b1;
+    if (i + 1 < n) {
+      an = xa[4 * (i + 1)];
+      b0n = wb0[4 * (i + 1)];
+      b1n = wb1[4 * (i + 1)];
+    }
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bv0[4] = {b0.x, b0.y, b0.z, b0.w};
+    const uint32_t bv1[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const double alo = bf16_lo(av[j]), ahi = bf16_hi(av[j]);
+      c0 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv0[j]), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv1[j]), c1, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv0[j]), d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv1[j]), d1, 0, 0, 0);
+    }
+    a = an, b0 = b0n, b1 = b1n;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int t = t0 + 4 * q + g;
+    if (t < T) {
+      logits[(size_t)t * E + e0 + r] = (float)(c0[q] + d0[q]);
+      logits[(size_t)t * E + e0 + 16 + r] = (float)(c1[q] + d1[q]);
+    }
+  }
+}
+
 hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t *wr,
                                 float *logits, hipStream_t s) {
   if (T <= 8) {
     const int waves = T * E;
     const int blocks = (waves + 3) / 4;
     k_router_gemv<<<blocks, 256, 0, s>>>(T, H, E, x, wr, logits);
+  } else if (E % 64 == 0 && H % 32 == 0) {
+    k_router_mfma<<<dim3(E / 64, (T + 31) / 32), 256, 0, s>>>(T, H, E, x, wr, logits);
   } else {
     dim3 grid((E + 63) / 64, (T + 31) / 32);
     k_router_gemm<<<grid, 256, 0, s>>>(T, H, E, x, wr, logits);
