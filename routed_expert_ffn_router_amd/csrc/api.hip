@@ -163,8 +163,8 @@ bool gemm_fits(int T, int H, int I, int n_rows) {
 }
 
 // the matrix cores pay once the buckets hold several rows each
-bool use_gemm(int T, int H, int I, int E, int n_rows, bool dense) {
-  if (!gemm_supported(H, I) || !gemm_fits(T, H, I, n_rows)) return false;
+bool use_gemm(int T, int H, int I, int E, int n_rows, bool dense, int fmt_gate, int fmt_down) {
+  if (!gemm_supported(H, I, fmt_gate, fmt_down) || !gemm_fits(T, H, I, n_rows)) return false;
   return dense ? n_rows >= 32 : (long long)n_rows >= 4LL * E;
 }
 
@@ -173,8 +173,8 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
             float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
   Marker none;
   Marker &m = mk ? *mk : none;
-  if (use_gemm(T, H, I, g.E, n_rows, !offsets))
-    return hip_check(launch_gemm_ffn(g, u, d, H, I, x, offsets, sorted_token, n_rows, b.tiles,
+  if (use_gemm(T, H, I, g.E, n_rows, !offsets, g.fmt, d.fmt))
+    return hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
                                      reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m),
                      "gemm ffn");
   if (!offsets) {
@@ -456,9 +456,9 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
-    if (use_gemm(T, H, L->I_shared, 1, T, true)) {
+    if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
       mk("shared_gemm");
-      MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, x, nullptr, nullptr, T,
+      MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
                                         b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh),
                                         b.shared_y, s, nullptr, nullptr),
                         "shared gemm"));

@@ -90,6 +90,7 @@ struct GemmArgs {
   const uint16_t *x;         // gate/up: bf16 tokens [T][K]
   const int32_t *row_token;  // gate/up: token of each bucket row (null: the row itself)
   const uint16_t *a16;       // down: fp16 SwiGLU output [n_rows][K]
+  int a_rows;                // rows of x (gate/up: T) or of a16 (down: n_rows)
   const int32_t *tiles;
   uint16_t *a_out;           // gate/up: fp16 [n_rows][N]
   float *y_out;              // down: fp32 [n_rows][N]
@@ -194,12 +195,8 @@ struct BStage {
 template <int MODE, int OP>
 struct AStage {
   uint32_t raw[8];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, bool valid, int k) {
-    if (!valid) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) raw[i] = 0;
-      return;
-    }
+  // rows past the bucket carry an offset beyond the buffer: the loads read zeros
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int k) {
     const uint32_t vo = row_off + (uint32_t)k * 2u;
     const u32x4_t q0 = buf_u128(r, vo, 0), q1 = buf_u128(r, vo + 16, 0);
     raw[0] = q0.x, raw[1] = q0.y, raw[2] = q0.z, raw[3] = q0.w;
@@ -263,27 +260,39 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 
   // A staging: bucket row tid / 4
   const int arow = tid >> 2, ak = (tid & 3) * 16;
-  const bool avalid = r0 + arow < r1;
-  uint32_t a_off = 0;
-  if (avalid) {
+  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)p.K * 2u;
+  uint32_t a_off = a_bytes;  // past the end: zeros
+  if (r0 + arow < r1) {
     const int src = (MODE == kModeGateUp && p.row_token) ? p.row_token[r0 + arow] : r0 + arow;
     a_off = (uint32_t)src * (uint32_t)p.K * 2u;
   }
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(MODE == kModeGateUp ? p.x : p.a16, 0x7FFFFFFF);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(MODE == kModeGateUp ? p.x : p.a16, a_bytes);
   // B staging: tile row tid / 2 (waves 2, 3 stage the up rows of a gate/up tile)
   const int brow = tid >> 1, bk = (tid & 1) * 32;
   const bool b_up = MODE == kModeGateUp && wave >= 2;
   const WView &bw = b_up ? p.w1 : p.w0;
   const int wrow = MODE == kModeGateUp ? n0 + (brow & (kBN / 2 - 1)) : n0 + brow;
 
-  AStage<MODE, OP> sa;
-  BStage<FMT, OP> sb;
+  // kPD stages in flight: stage s is staged in registers slot s % kPD from the
+  // time its loads are issued until it is decoded into LDS, kPD - 1 stages
+  // before the MFMAs read it, which covers the HBM latency
+  constexpr int kPD = 4;
+  AStage<MODE, OP> sa[kPD];
+  BStage<FMT, OP> sb[kPD];
   const int nk = p.K / kBK;
-  sa.load(ra, a_off, avalid, ak);
-  sb.load(bw, e, wrow, bk);
+#pragma unroll
+  for (int u = 0; u < kPD; u++) {  // nk >= kPD (K >= 256)
+    sa[u].load(ra, a_off, u * kBK + ak);
+    sb[u].load(bw, e, wrow, u * kBK + bk);
+  }
   if constexpr (FMT == MOE_FMT_VQ2) __syncthreads();
-  sa.store(&s_a[0][arow * kLdsW + ak / 2]);
-  sb.store(&s_b[0][brow * kLdsW + bk / 2], s_cb);
+  sa[0].store(&s_a[0][arow * kLdsW + ak / 2]);
+  sb[0].store(&s_b[0][brow * kLdsW + bk / 2], s_cb);
+  {  // stages past the end re-read the last one (never used; keeps the loads unconditional)
+    const int st = min(kPD, nk - 1);
+    sa[0].load(ra, a_off, st * kBK + ak);
+    sb[0].load(bw, e, wrow, st * kBK + bk);
+  }
   __syncthreads();
 
   // the lane's two B columns: gate/up -> (gate, up) of column n0 + 32 wn + lane % 32;
@@ -293,57 +302,76 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const int bc1 = MODE == kModeGateUp ? kBN / 2 + 32 * wn + cl : 64 * wn + 32 + cl;
   const int arow_frag = 32 * wm + cl;
   const int kh = 8 * (lane >> 5);
+  // a wave whose 32 rows all lie past the bucket's end skips its MFMAs
+  const bool active = r0 + 32 * wm < r1;
 
   constexpr bool kGroupScale = FMT == MOE_FMT_VQ2;
+  // VQ2: the fp16 scales of the lane's two weight rows, all K / 256 <= 16 groups
+  uint32_t gsc0[kGroupScale ? 8 : 1] = {}, gsc1[kGroupScale ? 8 : 1] = {};
+  if constexpr (kGroupScale) {
+    const int wr0 = n0 + (MODE == kModeGateUp ? 32 * wn + cl : 64 * wn + cl);
+    const int wr1 = MODE == kModeGateUp ? wr0 : wr0 + 32;
+    const WView &v1 = MODE == kModeGateUp ? p.w1 : p.w0;
+    const uint32_t sbb = (uint32_t)expert_scale_bytes(FMT, p.w0.N, p.w0.K);
+    const uint32_t rb = (uint32_t)(p.K / 256) * 2u;  // scale bytes per row
+    const __amdgpu_buffer_rsrc_t s0 = make_rsrc(p.w0.scales + (size_t)e * sbb, sbb);
+    const __amdgpu_buffer_rsrc_t s1 = make_rsrc(v1.scales + (size_t)e * sbb, sbb);
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      // past the row's K / 256 groups this reads the next row (or zeros past
+      // the expert): never used, and it keeps the loads unconditional
+      gsc0[q] = buf_u32(s0, (uint32_t)wr0 * rb + 4 * q, 0);
+      gsc1[q] = buf_u32(s1, (uint32_t)wr1 * rb + 4 * q, 0);
+    }
+  }
   f32x16_t acc0 = {}, acc1 = {}, part0 = {}, part1 = {};
-  for (int it = 0; it < nk; it++) {
-    const int cur = it & 1;
-    if (it + 1 < nk) {
-      sa.load(ra, a_off, avalid, (it + 1) * kBK + ak);
-      sb.load(bw, e, wrow, (it + 1) * kBK + bk);
-    }
-    const uint32_t *A = s_a[cur];
-    const uint32_t *B = s_b[cur];
+  for (int it0 = 0; it0 < nk; it0 += kPD) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ks++) {
-      const int kk = ks * 16 + kh;
-      const uint4 af = *reinterpret_cast<const uint4 *>(&A[arow_frag * kLdsW + kk / 2]);
-      const uint4 bf0 = *reinterpret_cast<const uint4 *>(&B[bc0 * kLdsW + kk / 2]);
-      const uint4 bf1 = *reinterpret_cast<const uint4 *>(&B[bc1 * kLdsW + kk / 2]);
-      if constexpr (kGroupScale) {
-        part0 = mfma32<OP>(af, bf0, part0);
-        part1 = mfma32<OP>(af, bf1, part1);
-      } else {
-        acc0 = mfma32<OP>(af, bf0, acc0);
-        acc1 = mfma32<OP>(af, bf1, acc1);
-      }
-    }
-    if constexpr (kGroupScale) {
-      if ((it + 1) % (256 / kBK) == 0) {  // a 256-column group is complete: scale and fold
-        const int kb = it / (256 / kBK);
-        const int wr0 = n0 + (MODE == kModeGateUp ? 32 * wn + cl : 64 * wn + cl);
-        const int wr1 = MODE == kModeGateUp ? wr0 : wr0 + 32;
-        const WView &v1 = MODE == kModeGateUp ? p.w1 : p.w0;
-        const uint32_t sbb = (uint32_t)expert_scale_bytes(FMT, p.w0.N, p.w0.K);
-        const uint32_t ng = (uint32_t)(p.K / 256);
-        const float d0 = f16_bits_to_f32(
-            buf_u16(make_rsrc(p.w0.scales + (size_t)e * sbb, sbb), ((uint32_t)wr0 * ng + kb) * 2u, 0));
-        const float d1 = f16_bits_to_f32(
-            buf_u16(make_rsrc(v1.scales + (size_t)e * sbb, sbb), ((uint32_t)wr1 * ng + kb) * 2u, 0));
+    for (int u = 0; u < kPD; u++) {
+      const int it = it0 + u;  // nk % kPD == 0 (K % 256 == 0)
+      const uint32_t *A = s_a[it & 1];
+      const uint32_t *B = s_b[it & 1];
+      if (active) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          acc0[i] = fmaf(d0, part0[i], acc0[i]);
-          acc1[i] = fmaf(d1, part1[i], acc1[i]);
-          part0[i] = 0.0f;
-          part1[i] = 0.0f;
+        for (int ks = 0; ks < kBK / 16; ks++) {
+          const int kk = ks * 16 + kh;
+          const uint4 af = *reinterpret_cast<const uint4 *>(&A[arow_frag * kLdsW + kk / 2]);
+          const uint4 bf0 = *reinterpret_cast<const uint4 *>(&B[bc0 * kLdsW + kk / 2]);
+          const uint4 bf1 = *reinterpret_cast<const uint4 *>(&B[bc1 * kLdsW + kk / 2]);
+          if constexpr (kGroupScale) {
+            part0 = mfma32<OP>(af, bf0, part0);
+            part1 = mfma32<OP>(af, bf1, part1);
+          } else {
+            acc0 = mfma32<OP>(af, bf0, acc0);
+            acc1 = mfma32<OP>(af, bf1, acc1);
+          }
+        }
+        if constexpr (kGroupScale) {
+          if ((it + 1) % (256 / kBK) == 0) {  // a 256-column group is complete: scale and fold
+            const int kb = it / (256 / kBK);
+            const uint32_t h0 = gsc0[kb >> 1], h1 = gsc1[kb >> 1];
+            const float d0 = f16_bits_to_f32((kb & 1) ? h0 >> 16 : h0 & 0xFFFFu);
+            const float d1 = f16_bits_to_f32((kb & 1) ? h1 >> 16 : h1 & 0xFFFFu);
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+              acc0[i] = fmaf(d0, part0[i], acc0[i]);
+              acc1[i] = fmaf(d1, part1[i], acc1[i]);
+              part0[i] = 0.0f;
+              part1[i] = 0.0f;
+            }
+          }
         }
       }
+      // decode stage it + 1 into the other buffer, then refill its slot
+      const int slot = (u + 1) % kPD;
+      // (after the last stage this fills the idle buffer with a repeat: unread)
+      sa[slot].store(&s_a[(it + 1) & 1][arow * kLdsW + ak / 2]);
+      sb[slot].store(&s_b[(it + 1) & 1][brow * kLdsW + bk / 2], s_cb);
+      const int st = min(it + 1 + kPD, nk - 1);
+      sa[slot].load(ra, a_off, st * kBK + ak);
+      sb[slot].load(bw, e, wrow, st * kBK + bk);
+      __syncthreads();
     }
-    if (it + 1 < nk) {
-      sa.store(&s_a[cur ^ 1][arow * kLdsW + ak / 2]);
-      sb.store(&s_b[cur ^ 1][brow * kLdsW + bk / 2], s_cb);
-    }
-    __syncthreads();
   }
 
   // result i of the lane: tile row 32 wm + (i % 4) + 8 (i / 4) + 4 (lane / 32)
@@ -366,7 +394,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 // host
 // ---------------------------------------------------------------------------
 
-bool gemm_supported(int H, int I) { return H >= 256 && I >= 256 && H % 256 == 0 && I % 256 == 0; }
+// K a multiple of 256 (whole Q2K / VQ2 groups; at least kPD stages); VQ2 keeps
+// all its K / 256 group scales of a row in registers: K <= 4096
+bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
+  if (H < 256 || I < 256 || H % 256 || I % 256) return false;
+  if (fmt_gate == MOE_FMT_VQ2 && H > 4096) return false;
+  if (fmt_down == MOE_FMT_VQ2 && I > 4096) return false;
+  return true;
+}
 
 namespace {
 
@@ -391,10 +426,10 @@ hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s
 }  // namespace
 
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
-                           const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
+                           int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
                            int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
                            void (*mark)(void *, const char *), void *mark_ctx) {
-  if (!gemm_supported(H, I) || n_rows < 1) return hipErrorInvalidValue;
+  if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
   const int E = offsets ? gate.E : 0;
   const int max_tiles = ((n_rows + kBM - 1) / kBM + E + 7) / 8 * 8;
   if (mark) mark(mark_ctx, "tile_list");
@@ -403,7 +438,7 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   if (err != hipSuccess) return err;
 
   GemmArgs g{};
-  g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x;
+  g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x, g.a_rows = T;
   g.row_token = offsets ? sorted_token : nullptr;
   g.tiles = tiles, g.a_out = a16;
   if (mark) mark(mark_ctx, "gemm_gateup");
@@ -412,7 +447,8 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
-  d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.a16 = a16, d.tiles = tiles, d.y_out = y;
+  d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.a16 = a16, d.a_rows = n_rows, d.tiles = tiles;
+  d.y_out = y;
   if (mark) mark(mark_ctx, "gemm_down");
   return gemm_fmt<kModeDown>(d, down.fmt, kOpF16, dim3(H / kBN, max_tiles), s);
 }

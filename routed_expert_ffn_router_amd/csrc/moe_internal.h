@@ -81,12 +81,12 @@ hipError_t launch_down_gemv(const WView &down, int H, int I, const float *a,
 
 // prefill grouped GEMMs (gemm.hip) --------------------------------------------
 // Whole expert FFN on the matrix cores: y[r] = down_e . SwiGLU(gate_e, up_e; x[tok[r]])
-// for every bucket row r (offsets null: one dense expert over rows [0, n_rows)).
+// for every bucket row r (offsets null: one dense expert over rows [0, n_rows = T)).
 // tiles: gemm_tile_ints(n_rows, offsets ? E : 0) ints; a16: fp16 [n_rows][I].
-bool gemm_supported(int H, int I);
+bool gemm_supported(int H, int I, int fmt_gate, int fmt_down);
 size_t gemm_tile_ints(int n_rows, int E);
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
-                           const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
+                           int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
                            int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
                            void (*mark)(void *, const char *), void *mark_ctx);
 
