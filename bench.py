@@ -50,7 +50,120 @@ def _args():
     ap.add_argument("--extras", default="prefill_2048",
                     help="comma-separated extra workloads measured after the headline")
     ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 4 times (HBM counter calibration) and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                       "COPY_WRITE_DIR"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs (this workload, then "
+                         "the copy probe) into profiles/traffic.json and exit")
+    ap.add_argument("--copy-mib", type=int, default=256)
     return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# HBM traffic from hardware counters
+# --------------------------------------------------------------------------
+
+# marker name -> substring of the HIP kernel's symbol
+KERNEL_OF = {"decode_p1": "k_dec_p1", "decode_p2": "k_dec_p2", "decode_p3": "k_dec_p3",
+             "router": "k_router", "gemm_gateup": "k_gemm<0, 2", "gemm_down": "k_gemm<1, 1",
+             "combine": "k_combine", "select": "k_select", "select_plan": "k_select_plan",
+             "routed_gateup": "k_gateup", "routed_down": "k_down", "shared_gateup": "k_gateup",
+             "shared_down": "k_down"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def sources_sha():
+    """Digest of every source the kernels are built from: counters recorded
+    against another digest describe other kernels and are not reported."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc", "*"))) + \
+        [os.path.join(ROOT, "include", "moe.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def _per_kernel(rows, counter):
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def pmc_summary(args):
+    fetch_d, write_d, cfetch_d, cwrite_d = args.pmc_summary
+    nbytes = args.copy_mib << 20
+    scale = {}
+    for name, d, ctr in (("fetch", cfetch_d, "FETCH_SIZE"), ("write", cwrite_d, "WRITE_SIZE")):
+        vals = [v for k, vs in _per_kernel(_pmc_rows(d), ctr).items() if "copyBuffer" in k for v in vs]
+        got = max(vals) * 1024.0  # KiB -> bytes, the probe's big copy
+        scale[name] = nbytes / got
+    fetch = _per_kernel(_pmc_rows(fetch_d), "FETCH_SIZE")
+    write = _per_kernel(_pmc_rows(write_d), "WRITE_SIZE")
+    kernels = {}
+    lines = [f"copy calibration: {args.copy_mib} MiB copy; FETCH_SIZE scale {scale['fetch']:.4f}, "
+             f"WRITE_SIZE scale {scale['write']:.4f}",
+             f"{'kernel':64s} {'launches':>8s} {'fetch MB':>10s} {'write MB':>10s} {'HBM MB':>10s}"]
+    for k in sorted(fetch, key=lambda k: -np.mean(fetch[k])):
+        if "copyBuffer" in k or "spin_kernel" in k or k not in write:
+            continue
+        f_b = float(np.mean(fetch[k])) * 1024.0 * scale["fetch"]
+        w_b = float(np.mean(write[k])) * 1024.0 * scale["write"]
+        kernels[k] = {"fetch_bytes": f_b, "write_bytes": w_b, "bytes": f_b + w_b,
+                      "launches": len(fetch[k])}
+        lines.append(f"{k[:64]:64s} {len(fetch[k]):8d} {f_b / 1e6:10.3f} {w_b / 1e6:10.3f} "
+                     f"{(f_b + w_b) / 1e6:10.3f}")
+    db = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            db = json.load(fh)
+    db[args.workload] = {"sources_sha": sources_sha(), "scale": scale, "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def measured_traffic(workload, marker):
+    """HBM bytes per launch of `marker`'s kernel from the committed counter
+    summary, or None when there is none or the kernels changed since."""
+    if not os.path.exists(TRAFFIC_FILE) or marker not in KERNEL_OF:
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        rec = json.load(fh).get(workload)
+    if not rec or rec.get("sources_sha") != sources_sha():
+        return None
+    hits = [v["bytes"] for k, v in rec["kernels"].items() if KERNEL_OF[marker] in k]
+    return hits[0] if len(hits) == 1 else None
+
+
+def copy_probe(mib):
+    import torch
+
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib}))
 
 
 # --------------------------------------------------------------------------
@@ -77,10 +190,14 @@ def kernel_cost(name, L, T, U, n):
         "router": (E * H * 2 + xb + T * E * 4, 2 * T * E * H),
         "shared_gateup": (2 * Is * H * 2 + xb + T * Is * 4, 4 * T * Is * H),
         "shared_down": (H * Is * 2 + T * Is * 4 + T * H * 4, 2 * T * H * Is),
-        "shared_gemm": (3 * Is * H * 2 + xb + 2 * T * Is * 2 + T * H * 4, 6 * T * H * Is),
+        "shared_tile_list": (0, 0),
+        "shared_gemm_gateup": (2 * Is * H * 2 + xb + T * Is * 2, 4 * T * Is * H),
+        "shared_gemm_down": (H * Is * 2 + T * Is * 2 + T * H * 4, 2 * T * H * Is),
         "select_plan": (T * E * 4 + n * 16, 0),
         "select": (T * E * 4 + n * 8, 0),
-        "dispatch": (n * 4 * 5, 0),
+        "dispatch_counts": (n * 4, 0),
+        "dispatch_scan": (2 * ((n + 255) // 256) * E * 4, 0),
+        "dispatch_scatter": (n * 4 * 4 + ((n + 255) // 256) * E * 4, 0),
         "plan": ((E + 1) * 4, 0),
         "tile_list": ((E + 1) * 4, 0),
         "routed_gateup": (U * gu + cb + xb + n * I * 4, 4 * n * I * H),
@@ -196,16 +313,19 @@ def time_steps(f, layers, xs, lgs, tids, steps, warmup, graph_steps, use_graph):
 
 
 def kernel_times(f, layers, xs, lgs, tids, steps):
-    """Average duration (s) of each kernel of a step, from HIP events that
-    moe_forward_marked records between its kernels on the launch stream."""
+    """Average duration (s) of each kernel of a step: moe_forward_marked launches
+    every kernel with a pair of HIP events that the launch itself records at the
+    kernel's start and end, on the stream the kernel runs on."""
     import torch
 
     R, P = len(layers), len(xs)
-    nmax = 16
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nmax)] for _ in range(steps)]
+    nmax = 24
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nmax)] for _ in range(steps)]
     for row in evs:  # torch creates the HIP event on first record
-        for ev in row:
-            ev.record()
+        for a, b in row:
+            a.record()
+            b.record()
     torch.cuda.synchronize()
     torch.cuda._sleep(60_000_000)  # keep the GPU busy while the host enqueues every step
     names = None
@@ -215,8 +335,9 @@ def kernel_times(f, layers, xs, lgs, tids, steps):
     torch.cuda.synchronize()
     acc = {}
     for i in range(steps):
-        for j in range(len(names) - 1):
-            acc.setdefault(names[j], []).append(evs[i][j].elapsed_time(evs[i][j + 1]) / 1e3)
+        for j, name in enumerate(names):
+            a, b = evs[i][j]
+            acc.setdefault(name, []).append(a.elapsed_time(b) / 1e3)
     return {k: float(np.mean(v[1:] if len(v) > 2 else v)) for k, v in acc.items()}
 
 
@@ -290,6 +411,9 @@ def w_is_decode(wname):
 
 def main():
     args = _args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "libmoe runs on one GPU: the layer is not sharded here "
                           "(see the sharding design note); run with --gpus 1"}))
@@ -298,8 +422,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     head, host, w, L = measure(args.workload, args, dev, True)
     roof = head["roofline"]
+    roof["traffic"] = measured_traffic(args.workload, roof["kernel"])
     extras = {}
     for name in [e for e in args.extras.split(",") if e and e != args.workload]:
         torch.cuda.empty_cache()

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum {
   MOE_OK = 0,
@@ -172,14 +172,16 @@ int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *l
                 int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                 void *stream);
 
-/* moe_forward_marked: moe_forward for measurement tools.  Before each
- * kernel it enqueues, and once after the last, it records the caller's event
- * marks[i].event (a hipEvent_t passed as void*) on `stream` and sets
- * marks[i].name to a static string naming the kernel that follows ("end"
- * for the last mark).  At most max_marks marks are recorded; *n_marks gets
- * the number recorded.  Results are identical to moe_forward. */
+/* moe_forward_marked: moe_forward for measurement tools.  Each kernel the
+ * call enqueues (up to max_marks of them) is launched so that it records the
+ * caller's events marks[i].start and marks[i].stop (hipEvent_t passed as
+ * void*) when it begins and ends on `stream` (HIP's extended launch), and
+ * marks[i].name is set to a static string naming that kernel.  *n_marks gets
+ * the number of kernels so timed.  Results are identical to moe_forward.
+ * Every event must be non-null (MOE_EINVAL otherwise). */
 typedef struct {
-  void *event;
+  void *start;
+  void *stop;
   const char *name;
 } moe_mark;
 int moe_forward_marked(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,

@@ -41,7 +41,7 @@ class Layer(C.Structure):
 
 
 class Mark(C.Structure):
-    _fields_ = [("event", C.c_void_p), ("name", C.c_char_p)]
+    _fields_ = [("start", C.c_void_p), ("stop", C.c_void_p), ("name", C.c_char_p)]
 
 
 _lib = None
@@ -299,10 +299,11 @@ class Forward:
 
 
     def marked(self, x, events, logits_in=None, token_ids=None, layer=None):
-        """moe_forward_marked: records torch.cuda.Event objects between kernels;
-        returns the kernel names (one per interval)."""
+        """moe_forward_marked: `events` is a list of (start, stop) torch.cuda.Event
+        pairs (already recorded once, so that the HIP events exist); kernel i
+        records pair i at its own start and end.  Returns the kernel names."""
         L = self.layer if layer is None else layer
-        marks = (Mark * len(events))(*[Mark(ev.cuda_event, None) for ev in events])
+        marks = (Mark * len(events))(*[Mark(a.cuda_event, b.cuda_event, None) for a, b in events])
         n = C.c_int(0)
         _check(lib().moe_forward_marked(C.byref(L.c), self.T, _ptr(x), _ptr(logits_in),
                                         _ptr(token_ids), _ptr(self.out), _ptr(self.out_bf16),

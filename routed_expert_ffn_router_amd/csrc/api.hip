@@ -113,23 +113,21 @@ int check_ffn_weights(int E, int H, int I, const moe_weights *gate, const moe_we
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
-// Optional event marks between kernels (moe_forward_marked).
+thread_local hipEvent_t t_start = nullptr, t_stop = nullptr;
+
+// Optional per-kernel timing (moe_forward_marked): each mark arms the next
+// launch to record marks[n].start / marks[n].stop at its own start and end.
 struct Marker {
   moe_mark *m = nullptr;
   int max = 0, n = 0;
-  hipStream_t s = nullptr;
-  hipError_t err = hipSuccess;
   void operator()(const char *name) {
     if (m && n < max) {
-      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(m[n].event), s);
-      if (e != hipSuccess) {
-        if (err == hipSuccess) err = e;
-        (void)hipGetLastError();  // do not leave it for the next launch check
-      }
+      timer_arm(static_cast<hipEvent_t>(m[n].start), static_cast<hipEvent_t>(m[n].stop));
       m[n].name = name;
       n++;
     }
   }
+  ~Marker() { timer_arm(nullptr, nullptr); }  // nothing stays armed past the call
 };
 
 void mark_cb(void *ctx, const char *name) { (*static_cast<Marker *>(ctx))(name); }
@@ -141,6 +139,10 @@ WView bf16_view(const uint16_t *p, int N, int K) {
 // ---------------------------------------------------------------------------
 // expert FFN workspace and sequence (shared by moe_expert_ffn and moe_forward)
 // ---------------------------------------------------------------------------
+
+const char *const kRoutedGemmNames[3] = {"tile_list", "gemm_gateup", "gemm_down"};
+const char *const kSharedGemmNames[3] = {"shared_tile_list", "shared_gemm_gateup",
+                                         "shared_gemm_down"};
 
 struct FfnBufs {
   int32_t *plan;
@@ -175,7 +177,8 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
   Marker &m = mk ? *mk : none;
   if (use_gemm(T, H, I, g.E, n_rows, !offsets, g.fmt, d.fmt))
     return hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
-                                     reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m),
+                                     reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m,
+                                     kRoutedGemmNames),
                      "gemm ffn");
   if (!offsets) {
     m("gateup_gemv");
@@ -278,6 +281,12 @@ int check_layer(const moe_layer *L) {
 }
 
 }  // namespace
+
+void moe::timer_arm(hipEvent_t start, hipEvent_t stop) { t_start = start, t_stop = stop; }
+void moe::timer_take(hipEvent_t *start, hipEvent_t *stop) {
+  *start = t_start, *stop = t_stop;
+  t_start = t_stop = nullptr;
+}
 
 // =============================================================================
 // C ABI
@@ -417,7 +426,6 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     return fail(MOE_ENOSPC, "forward workspace: %zu bytes < %zu", ws_bytes, need);
 
   hipStream_t s = as_stream(stream);
-  mk.s = s;
   const int E = L->E, k = L->k, H = L->H, I = L->I, n = T * k;
   Carver c(ws);
   FwdBufs b = carve_fwd(c, L, T, false, false, false);
@@ -441,9 +449,7 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     a.a_hi = reinterpret_cast<uint16_t *>(b.a);
     a.a_lo = a.a_hi + (size_t)k * I;
     a.topk_idx = idx, a.topk_w = w, a.out = out_f32, a.out_bf16 = out_bf16;
-    const int rc = hip_check(launch_decode1(a, s, mark_cb, &mk), "decode");
-    mk("end");
-    return rc;
+    return hip_check(launch_decode1(a, s, mark_cb, &mk), "decode");
   }
   const float *logits = logits_in;
   if (!logits) {
@@ -457,10 +463,9 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
     if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
-      mk("shared_gemm");
       MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
                                         b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh),
-                                        b.shared_y, s, nullptr, nullptr),
+                                        b.shared_y, s, mark_cb, &mk, kSharedGemmNames),
                         "shared gemm"));
     } else {
       mk("shared_gateup");
@@ -473,7 +478,6 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     }
   }
   const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
-  int rc;
   if (fwd_small(L, T)) {
     mk("select_plan");
     MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
@@ -486,27 +490,22 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     mk("routed_down");
     MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
     mk("combine");
-    rc = hip_check(
+    return hip_check(
         launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
         "combine");
-    mk("end");
-    return rc;
   }
   mk("select");
   MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
                                   nullptr, nullptr, nullptr, nullptr, nullptr, s),
                     "select"));
-  mk("dispatch");
   MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
-                                    b.slot_pos, b.dispatch_ws, s),
+                                    b.slot_pos, b.dispatch_ws, s, mark_cb, &mk),
                     "dispatch"));
   MOE_TRY(run_ffn(T, H, I, x, g, u, d, b.offsets, b.sorted_token, n, b.y_rows, b.ffn, s, &mk));
   mk("combine");
-  rc = hip_check(
+  return hip_check(
       launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
       "combine");
-  mk("end");
-  return rc;
 }
 
 int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
@@ -524,14 +523,13 @@ int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float
                        moe_mark *marks, int max_marks, int *n_marks, void *stream) {
   if (max_marks < 0 || (max_marks > 0 && !marks)) return fail(MOE_EINVAL, "bad marks");
   for (int i = 0; i < max_marks; i++)
-    if (!marks[i].event) return fail(MOE_EINVAL, "mark %d has no event", i);
+    if (!marks[i].start || !marks[i].stop) return fail(MOE_EINVAL, "mark %d lacks an event", i);
   Marker mk;
   mk.m = marks;
   mk.max = max_marks;
   const int rc = forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out,
                               topk_w_out, ws, ws_bytes, stream, mk);
   if (n_marks) *n_marks = mk.n;
-  if (rc == MOE_OK && mk.err != hipSuccess) return hip_check(mk.err, "event record");
   return rc;
 }
 

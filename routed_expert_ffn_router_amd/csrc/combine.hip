@@ -42,7 +42,7 @@ hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_
                           const float *w, const float *shared_y, float *out, uint16_t *out_bf16,
                           hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
-  k_combine<<<grid, 256, 0, s>>>(T, H, k, y_rows, slot_pos, w, shared_y, out, out_bf16);
+  launch(k_combine, dim3(grid), dim3(256), s, T, H, k, y_rows, slot_pos, w, shared_y, out, out_bf16);
   return hipGetLastError();
 }
 
@@ -86,7 +86,7 @@ hipError_t launch_dequant(const WView &w, int expert, int64_t w0, int64_t count,
                           hipStream_t s) {
   int64_t blocks = (count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  k_dequant<<<(unsigned)blocks, 256, 0, s>>>(w, expert, w0, count, out);
+  launch(k_dequant, dim3((unsigned)blocks), dim3(256), s, w, expert, w0, count, out);
   return hipGetLastError();
 }
 

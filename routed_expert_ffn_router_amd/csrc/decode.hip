@@ -203,7 +203,7 @@ int spl_of(int K) {
 
 template <int RFMT, int RSPL, int DSPL>
 hipError_t p2_launch(const DecodeArgs &a, hipStream_t s) {
-  k_dec_p2<RFMT, RSPL, DSPL><<<max(a.nb_routed, a.nb_shared_down), kDecThreads, 0, s>>>(a);
+  launch(k_dec_p2<RFMT, RSPL, DSPL>, dim3(max(a.nb_routed, a.nb_shared_down)), dim3(kDecThreads), s, a);
   return hipGetLastError();
 }
 
@@ -220,9 +220,9 @@ template <int DFMT>
 hipError_t p3_fmt(const DecodeArgs &a, int dspl, hipStream_t s) {
   const int grid = (a.H + kP3Rows - 1) / kP3Rows;
   if (dspl == 2)
-    k_dec_p3<DFMT, 2><<<grid, kDecThreads, 0, s>>>(a);
+    launch(k_dec_p3<DFMT, 2>, dim3(grid), dim3(kDecThreads), s, a);
   else if (dspl == 4)
-    k_dec_p3<DFMT, 4><<<grid, kDecThreads, 0, s>>>(a);
+    launch(k_dec_p3<DFMT, 4>, dim3(grid), dim3(kDecThreads), s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -265,9 +265,9 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
     mark(mark_ctx, "decode_p1");
     const int g1 = max(a.nb_router, a.nb_shared_gu);
     if (hs == 4)
-      k_dec_p1<4><<<g1, kDecThreads, 0, s>>>(a);
+      launch(k_dec_p1<4>, dim3(g1), dim3(kDecThreads), s, a);
     else
-      k_dec_p1<2><<<g1, kDecThreads, 0, s>>>(a);
+      launch(k_dec_p1<2>, dim3(g1), dim3(kDecThreads), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   mark(mark_ctx, "decode_p2");

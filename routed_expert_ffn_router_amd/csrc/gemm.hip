@@ -409,7 +409,7 @@ template <int MODE>
 hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s) {
 #define MOE_GEMM_CASE(F, O)                                \
   if (fmt == F && op == O) {                               \
-    k_gemm<MODE, F, O><<<grid, kGemmThreads, 0, s>>>(a);   \
+    launch(k_gemm<MODE, F, O>, dim3(grid), dim3(kGemmThreads), s, a);   \
     return hipGetLastError();                              \
   }
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpBF16)
@@ -428,12 +428,13 @@ hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                            int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
                            int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
-                           void (*mark)(void *, const char *), void *mark_ctx) {
+                           void (*mark)(void *, const char *), void *mark_ctx,
+                           const char *const names[3]) {
   if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
   const int E = offsets ? gate.E : 0;
   const int max_tiles = ((n_rows + kBM - 1) / kBM + E + 7) / 8 * 8;
-  if (mark) mark(mark_ctx, "tile_list");
-  k_tile_list<<<1, 1024, 0, s>>>(E, n_rows, offsets, tiles);
+  if (mark) mark(mark_ctx, names[0]);
+  launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, offsets, tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -441,7 +442,7 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x, g.a_rows = T;
   g.row_token = offsets ? sorted_token : nullptr;
   g.tiles = tiles, g.a_out = a16;
-  if (mark) mark(mark_ctx, "gemm_gateup");
+  if (mark) mark(mark_ctx, names[1]);
   err = gemm_fmt<kModeGateUp>(g, gate.fmt, gate.fmt == MOE_FMT_Q2K ? kOpF16 : kOpBF16,
                               dim3(I / (kBN / 2), max_tiles), s);
   if (err != hipSuccess) return err;
@@ -449,7 +450,7 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   GemmArgs d{};
   d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.a16 = a16, d.a_rows = n_rows, d.tiles = tiles;
   d.y_out = y;
-  if (mark) mark(mark_ctx, "gemm_down");
+  if (mark) mark(mark_ctx, names[2]);
   return gemm_fmt<kModeDown>(d, down.fmt, kOpF16, dim3(H / kBN, max_tiles), s);
 }
 

@@ -1,12 +1,40 @@
 // moe_internal.h -- host-side launchers shared between the libmoe sources.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "moe.h"
 
 namespace moe {
+
+// Measurement: a mark arms a pair of events that the next launch records at
+// its own start and end (HIP's extended launch); an unarmed launch records
+// nothing.  The arming is per host thread and consumed by that launch.
+void timer_arm(hipEvent_t start, hipEvent_t stop);
+void timer_take(hipEvent_t *start, hipEvent_t *stop);
+
+template <typename... P, size_t... I>
+inline void kernel_arg_ptrs(std::tuple<P...> &t, void **out, std::index_sequence<I...>) {
+  ((out[I] = static_cast<void *>(&std::get<I>(t))), ...);
+}
+
+// every libmoe kernel is launched through here
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A &&...a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> args{static_cast<P>(a)...};
+  void *ptrs[sizeof...(P) + 1];
+  kernel_arg_ptrs(args, ptrs, std::index_sequence_for<P...>{});
+  hipEvent_t ts, te;
+  timer_take(&ts, &te);
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s, ts,
+                            te, 0);
+}
 
 // A projection as the kernels see it.
 struct WView {
@@ -62,7 +90,8 @@ hipError_t launch_select(int mode, int T, int E, int k, const float *logits,
 size_t dispatch_ws_bytes(int T, int E, int k);
 hipError_t launch_dispatch(int T, int E, int k, const int32_t *idx, int32_t *offsets,
                            int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
-                           void *ws, hipStream_t s);
+                           void *ws, hipStream_t s, void (*mark)(void *, const char *) = nullptr,
+                           void *mark_ctx = nullptr);
 // compact plan from expert offsets (E+1 ints)
 hipError_t launch_plan_from_offsets(int E, const int32_t *offsets, int32_t *plan, hipStream_t s);
 
@@ -88,7 +117,8 @@ size_t gemm_tile_ints(int n_rows, int E);
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                            int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
                            int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
-                           void (*mark)(void *, const char *), void *mark_ctx);
+                           void (*mark)(void *, const char *), void *mark_ctx,
+                           const char *const names[3]);
 
 // fused batch-1 decode (decode.hip) ------------------------------------------
 struct DecodeArgs {

@@ -155,12 +155,12 @@ hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const ui
   if (T <= 8) {
     const int waves = T * E;
     const int blocks = (waves + 3) / 4;
-    k_router_gemv<<<blocks, 256, 0, s>>>(T, H, E, x, wr, logits);
+    launch(k_router_gemv, dim3(blocks), dim3(256), s, T, H, E, x, wr, logits);
   } else if (E % 64 == 0 && H % 32 == 0) {
-    k_router_mfma<<<dim3(E / 64, (T + 31) / 32), 256, 0, s>>>(T, H, E, x, wr, logits);
+    launch(k_router_mfma, dim3(E / 64, (T + 31) / 32), dim3(256), s, T, H, E, x, wr, logits);
   } else {
     dim3 grid((E + 63) / 64, (T + 31) / 32);
-    k_router_gemm<<<grid, 256, 0, s>>>(T, H, E, x, wr, logits);
+    launch(k_router_gemm, dim3(grid), dim3(256), s, T, H, E, x, wr, logits);
   }
   return hipGetLastError();
 }
@@ -277,10 +277,10 @@ hipError_t launch_select(int mode, int T, int E, int k, const float *logits,
                          int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
                          float *row_w, int32_t *plan, hipStream_t s) {
   if (sorted_token) {
-    k_select_plan<<<1, 1024, 0, s>>>(mode, T, E, k, logits, token_ids, idx, w, offsets,
+    launch(k_select_plan, dim3(1), dim3(1024), s, mode, T, E, k, logits, token_ids, idx, w, offsets,
                                      sorted_token, sorted_slot, slot_pos, row_w, plan);
   } else {
-    k_select<<<(T + 3) / 4, 256, 0, s>>>(mode, T, E, k, logits, token_ids, idx, w);
+    launch(k_select, dim3((T + 3) / 4), dim3(256), s, mode, T, E, k, logits, token_ids, idx, w);
   }
   return hipGetLastError();
 }
@@ -355,14 +355,18 @@ size_t dispatch_ws_bytes(int T, int E, int k) {
 
 hipError_t launch_dispatch(int T, int E, int k, const int32_t *idx, int32_t *offsets,
                            int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
-                           void *ws, hipStream_t s) {
+                           void *ws, hipStream_t s, void (*mark)(void *, const char *),
+                           void *mark_ctx) {
   const int n = T * k;
   const int nchunks = (n + kChunk - 1) / kChunk;
   int32_t *counts = static_cast<int32_t *>(ws);
-  k_chunk_counts<<<nchunks, kChunk, 0, s>>>(n, E, idx, counts);
-  k_chunk_scan<<<1, 1024, 0, s>>>(n, nchunks, E, counts, offsets);
-  k_chunk_scatter<<<nchunks, kChunk, 0, s>>>(n, E, k, idx, counts, sorted_token, sorted_slot,
-                                             slot_pos);
+  if (mark) mark(mark_ctx, "dispatch_counts");
+  launch(k_chunk_counts, dim3(nchunks), dim3(kChunk), s, n, E, idx, counts);
+  if (mark) mark(mark_ctx, "dispatch_scan");
+  launch(k_chunk_scan, dim3(1), dim3(1024), s, n, nchunks, E, counts, offsets);
+  if (mark) mark(mark_ctx, "dispatch_scatter");
+  launch(k_chunk_scatter, dim3(nchunks), dim3(kChunk), s, n, E, k, idx, counts, sorted_token,
+         sorted_slot, slot_pos);
   return hipGetLastError();
 }
 
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(1024) void k_plan_from_offsets(int E, const int32_t
 }
 
 hipError_t launch_plan_from_offsets(int E, const int32_t *offsets, int32_t *plan, hipStream_t s) {
-  k_plan_from_offsets<<<1, 1024, 0, s>>>(E, offsets, plan);
+  launch(k_plan_from_offsets, dim3(1), dim3(1024), s, E, offsets, plan);
   return hipGetLastError();
 }
 

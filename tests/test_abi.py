@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
 
 
 def _w(fmt=moe.FMT_VQ2, E=8, N=2048, K=4096, data=FAKE, scales=FAKE, cb=FAKE):
