@@ -184,9 +184,9 @@ def kernel_cost(name, L, T, U, n):
         # select + routed gate/up, (3) routed down + combine
         "decode_p1": (2 * Is * H * 2 + E * H * 2 + xb + Is * 4 + E * 4,
                       2 * T * (2 * Is * H + E * H)),
-        "decode_p2": (H * Is * 2 + U * gu + cb + xb + Is * 4 + E * 4 + T * H * 4 + n * I * 4 + n * 8,
-                      2 * T * H * Is + 4 * n * I * H),
-        "decode_p3": (U * dn + n * I * 4 + n * 8 + 2 * T * H * 4, 2 * n * H * I),
+        "decode_p2": (U * gu + cb + xb + E * 4 + n * I * 4 + n * 8, 4 * n * I * H),
+        "decode_p3": (U * dn + H * Is * 2 + Is * 4 + n * I * 4 + n * 8 + T * H * 4,
+                      2 * n * H * I + 2 * T * H * Is),
         "router": (E * H * 2 + xb + T * E * 4, 2 * T * E * H),
         "shared_gateup": (2 * Is * H * 2 + xb + T * Is * 4, 4 * T * Is * H),
         "shared_down": (H * Is * 2 + T * Is * 4 + T * H * 4, 2 * T * H * Is),

@@ -132,7 +132,6 @@ struct DecodeArgs {
   float *logits;             // [E]
   float *a_sh;               // [Is] (also holds a_sh_hi / a_sh_lo)
   uint16_t *a_sh_hi, *a_sh_lo;  // [Is] bf16 split of the shared SwiGLU output
-  float *shared_y;           // [H]
   float *a;                  // [k][I] (also holds a_hi / a_lo)
   uint16_t *a_hi, *a_lo;     // [k][I] bf16 split of the routed SwiGLU output
   int a_mode;                // how a is stored (set by launch_decode1)
@@ -140,7 +139,7 @@ struct DecodeArgs {
   float *topk_w;             // [k]
   float *out;                // [H]
   uint16_t *out_bf16;        // optional [H]
-  int nb_router, nb_shared_gu, nb_routed, nb_shared_down, tiles_per_expert;
+  int nb_router, nb_shared_gu, nb_routed, tiles_per_expert;
 };
 
 bool decode1_supported(int H, int I, int Is, int k);

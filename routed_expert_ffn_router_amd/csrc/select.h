@@ -23,10 +23,27 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 
 __device__ __forceinline__ float order_val(float v) { return v != v ? -INFINITY : v; }
 
+// The logits a wave needs for one token, loaded up front so that the selection
+// costs one memory round trip: candidate e = lane + 64 i sits in v[i].
+template <int NC>
+struct Logits {
+  float v[NC];
+  // candidates past E read entry E - 1 (no branch around the loads); the
+  // selection never takes them
+  __device__ __forceinline__ void load(int E, const float *__restrict__ l) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NC; i++) v[i] = l[min(lane + 64 * i, E - 1)];
+  }
+};
+
 // Lane j < k returns choice j in (*e_out, *w_out); other lanes get e = -1.
-// E <= kMaxE; every lane of the wave must call this.
-__device__ __forceinline__ void select_wave(int mode, int E, int k, const float *__restrict__ l,
-                                            int64_t tid, int *e_out, float *w_out) {
+// E <= 64 * NC; every lane of the wave must call this.  Softmax top-k reads
+// only the preloaded logits; hash routing reads the k selected ones.
+template <int NC>
+__device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits<NC> &lg,
+                                            const float *__restrict__ l, int64_t tid, int *e_out,
+                                            float *w_out) {
   const int lane = threadIdx.x & 63;
   int my_e = -1;
   float my_l = -INFINITY;
@@ -37,16 +54,15 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const float 
       my_l = l[my_e];
     }
   } else {
-    constexpr int NC = kMaxE / 64;
     float v[NC];
     uint32_t taken = 0;  // bit i: candidate lane + 64 i is taken or absent
 #pragma unroll
     for (int i = 0; i < NC; i++) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? order_val(l[e]) : -INFINITY;
-      if (e >= E) taken |= 1u << i;
+      v[i] = lane + 64 * i < E ? order_val(lg.v[i]) : -INFINITY;
+      if (lane + 64 * i >= E) taken |= 1u << i;
     }
     for (int j = 0; j < k; j++) {
+      // this lane's best free candidate (ties to its lower slot)
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
 #pragma unroll
@@ -58,11 +74,29 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const float 
         }
       }
       const float m = wave_max_f(bv);
-      const int e = wave_min_i((bi != 0x7FFFFFFF && bv == m) ? bi : 0x7FFFFFFF);
-      if ((e & 63) == lane) taken |= 1u << (e >> 6);
+      // the lanes holding the maximum; one of them is the rule's choice unless
+      // several tie, when the lowest expert index among them wins
+      const uint64_t tied = __ballot(bi != 0x7FFFFFFF && bv == m);
+      int e;
+      if ((tied & (tied - 1)) == 0)
+        e = __builtin_amdgcn_readlane(bi, __builtin_ctzll(tied));
+      else
+        e = wave_min_i((bi != 0x7FFFFFFF && bv == m) ? bi : 0x7FFFFFFF);
+      const int owner = e & 63, slot = e >> 6;
+      if (owner == lane) taken |= 1u << slot;
+      // the raw logit of the winner: m itself unless the maximum is -inf (then
+      // it may be a NaN, taken from its owner's register)
+      float raw = m;
+      if (m == -INFINITY) {
+        float r = lg.v[0];
+#pragma unroll
+        for (int i = 1; i < NC; i++)
+          if (i == slot) r = lg.v[i];
+        raw = __shfl(r, owner, 64);
+      }
       if (lane == j) {
         my_e = e;
-        my_l = l[e];
+        my_l = raw;
       }
     }
   }
@@ -72,6 +106,20 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const float 
   const float den = wave_sum_f(ex);
   *e_out = my_e;
   *w_out = ex / den;
+}
+
+// convenience: load and select (E <= kMaxE)
+__device__ __forceinline__ void select_wave(int mode, int E, int k, const float *__restrict__ l,
+                                            int64_t tid, int *e_out, float *w_out) {
+  if (E <= 256) {
+    Logits<4> lg;
+    if (mode != MOE_ROUTE_HASH) lg.load(E, l);
+    select_wave<4>(mode, E, k, lg, l, tid, e_out, w_out);
+  } else {
+    Logits<kMaxE / 64> lg;
+    if (mode != MOE_ROUTE_HASH) lg.load(E, l);
+    select_wave<kMaxE / 64>(mode, E, k, lg, l, tid, e_out, w_out);
+  }
 }
 
 }  // namespace moe
