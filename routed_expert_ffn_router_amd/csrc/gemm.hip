@@ -1,54 +1,62 @@
-// gemm.hip -- prefill: grouped per-expert GEMMs on the matrix cores.
+// gemm.hip -- batched tokens: grouped per-expert GEMMs on the matrix cores.
 //
-// With many tokens every expert receives a bucket of rows and the expert FFN
-// becomes a grouped GEMM (the ds4 pages: prefill amortises the expert weights
-// over the batch -- hysenlabs.com "SSD streaming"; matrix-instruction expert
-// kernels on newer devices -- hysenlabs.com "Model support and quantization").
-// Each workgroup computes a 64-row x 128-column tile of one expert's bucket:
-// the A rows (tokens gathered through the bucket, or the SwiGLU output in
-// bucket order) and the weight tile are staged through LDS, the weights being
-// dequantized as they are staged; 4 waves each run 32x32x16 MFMAs on a
-// 32 x 64 sub-tile.
+// With several tokens per expert the expert FFN becomes a grouped GEMM (the
+// ds4 pages: prefill amortises the expert weights over the batch --
+// hysenlabs.com "SSD streaming"; matrix-instruction expert kernels on newer
+// devices -- hysenlabs.com "Model support and quantization").  Each workgroup
+// computes BM bucket rows of one expert against 256 weight rows (gate/up: 128
+// gate + 128 up; down: 256 outputs): BM = 64 for prefill, 16 for skinny
+// batches.  Each of the 4 waves owns 64 weight rows for all BM rows and
+// dequantizes them straight into MFMA operand registers -- every weight is
+// decoded once per tile and never passes through LDS; only the activation
+// rows (gathered tokens, or the SwiGLU output in bucket order) are staged in
+// LDS and shared by the waves.  v_mfma_f32_16x16x32 throughout.
 //
-// Precision: gate/up multiply the bf16 tokens by exact bf16 weight values --
-// VQ2 codebook entries are small integers (exact in bf16) and the fp16 scale
-// of each 256-column group multiplies the fp32 partial sum of that group;
-// MXFP4 and bf16 weights are exact in bf16.  Q2K gate/up and every down
-// projection use fp16 operands (the SwiGLU output and the weights rounded to
-// fp16), accumulating in fp32.
+// K is walked in stages of 64.  In stage s, lane l of a wave covers the 16
+// consecutive weights k = 64 s + 16 (l / 16) + [0, 16) of its row (the MFMA's
+// reduction slots are a relabelling of k; A and B use the same one), so a
+// lane decodes exactly one Q2K sub-block, four VQ2 codes or eight MXFP4 bytes
+// per row and stage.
+//
+// Operand precision: bf16 tokens x exact bf16 weights for MXFP4 and bf16
+// gate/up; fp16 for VQ2 and Q2K gate/up (tokens converted exactly, weights
+// rounded once to fp16) and for every down projection (the SwiGLU output in
+// fp16).  Accumulation in fp32.
 #include "gemv_core.h"
 
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 64;          // bucket rows per tile
-constexpr int kBN = 128;         // weight rows per tile (gate/up: 64 gate + 64 up)
-constexpr int kBK = 64;          // reduction columns per stage
-constexpr int kLdsK = kBK + 8;   // padded LDS row: 144 bytes
-constexpr int kLdsW = kLdsK / 2; // ... in dwords
+constexpr int kBKs = 64;                  // K per stage
+constexpr int kLdsRow = kBKs + 8;         // padded LDS row (16-bit elements): 144 bytes
+constexpr int kLdsRowW = kLdsRow / 2;     // ... in dwords
 constexpr int kGemmThreads = 256;
+constexpr int kWRowsPerWave = 64;         // weight rows per wave (4 MFMA column blocks)
+constexpr int kWRows = 4 * kWRowsPerWave; // per block
+constexpr int kMinBM = 16;
 
 enum { kOpBF16 = 0, kOpF16 = 1 };
 enum { kModeGateUp = 0, kModeDown = 1 };
 
 // tile list: tiles[0] = count; tile i = tiles[1 + 3i .. 3 + 3i] = {expert, r0, r1}
 size_t gemm_tile_ints(int n_rows, int E) {
-  return 1 + 3 * (size_t)((n_rows + kBM - 1) / kBM + E);
+  return 1 + 3 * (size_t)((n_rows + kMinBM - 1) / kMinBM + E);
 }
 
-__global__ __launch_bounds__(1024) void k_tile_list(int E, int n_dense,
+__global__ __launch_bounds__(1024) void k_tile_list(int E, int n_dense, int bm,
                                                      const int32_t *__restrict__ offsets,
                                                      int32_t *__restrict__ tiles) {
   __shared__ int s_tmp[16];
   if (!offsets) {  // one dense expert over rows [0, n_dense)
-    const int n = (n_dense + kBM - 1) / kBM;
+    const int n = (n_dense + bm - 1) / bm;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       tiles[1 + 3 * i] = 0;
-      tiles[2 + 3 * i] = i * kBM;
-      tiles[3 + 3 * i] = min(n_dense, (i + 1) * kBM);
+      tiles[2 + 3 * i] = i * bm;
+      tiles[3 + 3 * i] = min(n_dense, (i + 1) * bm);
     }
     if (threadIdx.x == 0) tiles[0] = n;
     return;
@@ -58,7 +66,7 @@ __global__ __launch_bounds__(1024) void k_tile_list(int E, int n_dense,
   for (int e0 = 0; e0 < E; e0 += 1024) {
     const int e = e0 + threadIdx.x;
     const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (c + kBM - 1) / kBM;
+    const int nt = (c + bm - 1) / bm;
     int inc = nt;  // inclusive scan over the wave
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(inc, o, 64);
@@ -74,10 +82,10 @@ __global__ __launch_bounds__(1024) void k_tile_list(int E, int n_dense,
     __syncthreads();
     int pos = base + wbase + inc - nt;
     for (int t = 0; t < nt; t++, pos++) {
-      const int r0 = offsets[e] + t * kBM;
+      const int r0 = offsets[e] + t * bm;
       tiles[1 + 3 * pos] = e;
       tiles[2 + 3 * pos] = r0;
-      tiles[3 + 3 * pos] = min(offsets[e + 1], r0 + kBM);
+      tiles[3 + 3 * pos] = min(offsets[e + 1], r0 + bm);
     }
     base += tot;
   }
@@ -100,166 +108,222 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
-__device__ __forceinline__ uint32_t pack_b2(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
-}
-template <int OP>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return OP == kOpF16 ? pack_h2(a, b) : pack_b2(a, b);
-}
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) { return pack_h2(bf16_lo(v), bf16_hi(v)); }
 
 // ---------------------------------------------------------------------------
-// B (weight) stage: 128 weight rows x 64 columns.  Thread t stages row t / 2,
-// columns (t % 2) * 32 .. +32: it loads the packed bytes for the next stage
-// while the MFMAs of the current one run, then decodes them into 16 dwords of
-// operand pairs in LDS.
+// B: the weights of one row that a lane covers, raw bits -> operand pairs.
+//
+// K is cut into groups of 256 (one Q2K super-block, one VQ2 scale group) and
+// each group into 4 stages.  Stage s of a group holds the columns 64 j + 16 s
+// + [0, 16), j = 0..3, and lane group g = lane / 16 takes chunk j = g: over
+// the 4 stages of a group it covers the contiguous run 64 g + [0, 64) of its
+// row, which it loads at once (VQ2: 16 bytes of codes and the group's scale;
+// Q2K: 16 bytes of 2-bit codes, its 4 sub-blocks' scale bytes and d|dmin;
+// MXFP4: 32 bytes and 2 scales).  bf16 weights (64 bytes a run) are loaded
+// per stage instead.
 // ---------------------------------------------------------------------------
 template <int FMT, int OP>
-struct BStage {
-  uint32_t raw[FMT == MOE_FMT_BF16 ? 16 : 8];
-  uint32_t aux;
+struct BGroup {
+  uint32_t q[FMT == MOE_FMT_MXFP4 ? 8 : 4];
+  uint32_t s0, s1;  // VQ2: fp16 scale; Q2K: 4 scale/min bytes, d|dmin; MXFP4: 2 E8M0 bytes
 
-  __device__ __forceinline__ void load(const WView &w, int e, int row, int k) {
+  // k0: first column of the lane's run (a multiple of 64)
+  __device__ __forceinline__ void load(const WView &w, int e, int row, int k0) {
     const uint32_t db = (uint32_t)expert_data_bytes(FMT, w.N, w.K);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(w.data + (size_t)e * db, db);
-    if constexpr (FMT == MOE_FMT_BF16) {
-      const uint32_t vo = ((uint32_t)row * (uint32_t)w.K + (uint32_t)k) * 2u;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const u32x4_t q = buf_u128(r, vo + 16 * i, 0);
-        raw[4 * i] = q.x, raw[4 * i + 1] = q.y, raw[4 * i + 2] = q.z, raw[4 * i + 3] = q.w;
-      }
-    } else if constexpr (FMT == MOE_FMT_VQ2) {  // one code byte per 4 weights
-      const u32x2_t q = buf_u64(r, (uint32_t)row * (uint32_t)(w.K / 4) + (uint32_t)k / 4, 0);
-      raw[0] = q.x, raw[1] = q.y;
-    } else if constexpr (FMT == MOE_FMT_Q2K) {  // sub-blocks j, j+1 of one super-block
-      const uint32_t blk = ((uint32_t)row * (uint32_t)(w.K / 256) + (uint32_t)k / 256) * kQ2KBytes;
-      const uint32_t j = (k % 256) / 16;
-      raw[0] = buf_u32(r, blk + 16 + 4 * j, 0);
-      raw[1] = buf_u32(r, blk + 16 + 4 * j + 4, 0);
-      raw[2] = buf_u32(r, blk + 80, 0);
-      aux = buf_u16(r, blk + j, 0);
-    } else {  // MXFP4: 16 bytes of nibbles + one E8M0 scale per 32
+    if constexpr (FMT == MOE_FMT_VQ2) {
       const uint32_t sb = (uint32_t)expert_scale_bytes(FMT, w.N, w.K);
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.scales + (size_t)e * sb, sb);
-      const u32x4_t q = buf_u128(r, (uint32_t)row * (uint32_t)(w.K / 2) + (uint32_t)k / 2, 0);
-      raw[0] = q.x, raw[1] = q.y, raw[2] = q.z, raw[3] = q.w;
-      aux = buf_u8(rs, (uint32_t)row * (uint32_t)(w.K / 32) + (uint32_t)k / 32, 0);
+      const u32x4_t v = buf_u128(r, (uint32_t)row * (uint32_t)(w.K / 4) + (uint32_t)k0 / 4, 0);
+      q[0] = v.x, q[1] = v.y, q[2] = v.z, q[3] = v.w;
+      s0 = buf_u16(rs, ((uint32_t)row * (uint32_t)(w.K / 256) + (uint32_t)k0 / 256) * 2u, 0);
+    } else if constexpr (FMT == MOE_FMT_Q2K) {
+      const uint32_t blk = ((uint32_t)row * (uint32_t)(w.K / 256) + (uint32_t)k0 / 256) * kQ2KBytes;
+      const uint32_t j = (k0 % 256) / 16;  // first of the 4 sub-blocks
+      // (84-byte blocks keep only 4-byte alignment: dword loads)
+      q[0] = buf_u32(r, blk + 16 + 4 * j, 0);
+      q[1] = buf_u32(r, blk + 20 + 4 * j, 0);
+      q[2] = buf_u32(r, blk + 24 + 4 * j, 0);
+      q[3] = buf_u32(r, blk + 28 + 4 * j, 0);
+      s0 = buf_u32(r, blk + j, 0);
+      s1 = buf_u32(r, blk + 80, 0);
+    } else {  // MXFP4
+      const uint32_t sb = (uint32_t)expert_scale_bytes(FMT, w.N, w.K);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.scales + (size_t)e * sb, sb);
+      const uint32_t vo = (uint32_t)row * (uint32_t)(w.K / 2) + (uint32_t)k0 / 2;
+      const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+      q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w, q[4] = b.x, q[5] = b.y, q[6] = b.z, q[7] = b.w;
+      s0 = buf_u16(rs, (uint32_t)row * (uint32_t)(w.K / 32) + (uint32_t)k0 / 32, 0);
     }
   }
 
-  __device__ __forceinline__ void store(uint32_t *dst, const uint2 *s_cb) const {
-    uint32_t o[16];
-    if constexpr (FMT == MOE_FMT_BF16) {
+  // stage S of the group: the run's weights 16 S .. 16 S + 15; out[i] holds
+  // weights (2i, 2i + 1) of those as an OP pair
+  __device__ __forceinline__ void decode(int S, uint32_t (&out)[8], const uint2 *cb) const {
+    if constexpr (FMT == MOE_FMT_VQ2) {
+      // fp16 codebook integers (exact) times the fp16 scale, rounded once
+      const f16x2_t d2 = {__builtin_bit_cast(_Float16, (uint16_t)s0),
+                          __builtin_bit_cast(_Float16, (uint16_t)s0)};
 #pragma unroll
-      for (int i = 0; i < 16; i++) o[i] = OP == kOpF16 ? bf16x2_to_f16x2(raw[i]) : raw[i];
-    } else if constexpr (FMT == MOE_FMT_VQ2) {  // codebook integers; the group scale comes later
-#pragma unroll
-      for (int c = 0; c < 8; c++) {
-        const uint2 v = s_cb[(raw[c / 4] >> (8 * (c % 4))) & 255u];
-        o[2 * c] = v.x, o[2 * c + 1] = v.y;
+      for (int c = 0; c < 4; c++) {
+        const uint2 v = cb[((q[S] >> (8 * c)) & 255u) * kNCopy];
+        out[2 * c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * d2);
+        out[2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * d2);
       }
     } else if constexpr (FMT == MOE_FMT_Q2K) {
-      const float d = f16_bits_to_f32(raw[2] & 0xFFFFu), dmin = f16_bits_to_f32(raw[2] >> 16);
+      // the sub-block's four possible weights (q = 0..3), exact in fp32 up to
+      // the final subtraction, rounded to fp16: a byte lookup table
+      const uint32_t scm = (s0 >> (8 * S)) & 255u;
+      const float d = f16_bits_to_f32(s1 & 0xFFFFu), dmin = f16_bits_to_f32(s1 >> 16);
+      const float ds = d * (float)(scm & 15u), ms = dmin * (float)(scm >> 4);
+      const uint32_t lut_lo = pack_h2(-ms, ds - ms);
+      const uint32_t lut_hi = pack_h2(2.0f * ds - ms, 3.0f * ds - ms);
+      // selector bytes 2q, 2q + 1 of each weight pair: weight 4b + t sits in
+      // bits 8b + 2t of the dword
+      const uint32_t x = q[S];
+      const uint32_t el = (x << 1) & 0x06060606u;  // byte b: 2 q(4b)
+      const uint32_t ol = (x >> 1) & 0x06060606u;  // byte b: 2 q(4b+1)
+      const uint32_t eh = (x >> 3) & 0x06060606u;  // byte b: 2 q(4b+2)
+      const uint32_t oh = (x >> 5) & 0x06060606u;  // byte b: 2 q(4b+3)
 #pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const uint32_t scm = (aux >> (8 * s)) & 255u;
-        const float ds = d * (float)(scm & 15u), ms = dmin * (float)(scm >> 4);
+      for (int b = 0; b < 4; b++) {
+        const uint32_t sel_b = (uint32_t)b * 0x01010101u + 0x04040000u;  // bytes b, b, 4+b, 4+b
+        const uint32_t s_lo = __builtin_amdgcn_perm(ol, el, sel_b) | 0x01000100u;
+        const uint32_t s_hi = __builtin_amdgcn_perm(oh, eh, sel_b) | 0x01000100u;
+        out[2 * b] = __builtin_amdgcn_perm(lut_hi, lut_lo, s_lo);
+        out[2 * b + 1] = __builtin_amdgcn_perm(lut_hi, lut_lo, s_hi);
+      }
+    } else {  // MXFP4: E2M1 x 2^(e - 127), converted with the scale applied
+      const float sc = e8m0_to_f32((s0 >> (8 * (S / 2))) & 255u);
 #pragma unroll
-        for (int p = 0; p < 16; p += 2) {
-          const float w0 = ds * (float)((raw[s] >> (2 * p)) & 3u) - ms;
-          const float w1 = ds * (float)((raw[s] >> (2 * p + 2)) & 3u) - ms;
-          o[8 * s + p / 2] = pack2<OP>(w0, w1);
+      for (int j = 0; j < 2; j++) {
+        const uint32_t v = q[2 * S + j];
+        if constexpr (OP == kOpBF16) {
+          out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
+          out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
+          out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
+          out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
+        } else {
+          out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 0));
+          out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 1));
+          out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 2));
+          out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 3));
         }
       }
-    } else {  // MXFP4
-      const float sc = e8m0_to_f32(aux);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const uint32_t p0 = e2m1x2_to_bf16x2<0>(raw[j]), p1 = e2m1x2_to_bf16x2<1>(raw[j]);
-        const uint32_t p2 = e2m1x2_to_bf16x2<2>(raw[j]), p3 = e2m1x2_to_bf16x2<3>(raw[j]);
-        o[4 * j] = pack2<OP>(bf16_lo(p0) * sc, bf16_hi(p0) * sc);
-        o[4 * j + 1] = pack2<OP>(bf16_lo(p1) * sc, bf16_hi(p1) * sc);
-        o[4 * j + 2] = pack2<OP>(bf16_lo(p2) * sc, bf16_hi(p2) * sc);
-        o[4 * j + 3] = pack2<OP>(bf16_lo(p3) * sc, bf16_hi(p3) * sc);
-      }
     }
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-#pragma unroll
-    for (int i = 0; i < 4; i++) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
 };
 
-// A stage: 64 rows x 64 columns; thread t stages row t / 4, columns (t % 4) * 16 .. +16
-template <int MODE, int OP>
+// bf16 weights: one stage's 16 weights of the row (the run 64 g + 16 S + [0, 16))
+template <int OP>
+struct BStageBf16 {
+  uint32_t q[8];
+  __device__ __forceinline__ void load(const WView &w, int e, int row, int k) {
+    const uint32_t db = (uint32_t)expert_data_bytes(MOE_FMT_BF16, w.N, w.K);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(w.data + (size_t)e * db, db);
+    const uint32_t vo = ((uint32_t)row * (uint32_t)w.K + (uint32_t)k) * 2u;
+    const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+    q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w, q[4] = b.x, q[5] = b.y, q[6] = b.z, q[7] = b.w;
+  }
+  __device__ __forceinline__ void decode(uint32_t (&out)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = OP == kOpF16 ? bf16x2_to_f16x2(q[i]) : q[i];
+  }
+};
+
+// A stage: BM rows x 64 columns; thread t stages row t / (256 / BM), a run of
+// 64 * BM / 256 columns; rows past the bucket read zeros (an offset past the
+// buffer)
+template <int MODE, int OP, int BM>
 struct AStage {
-  uint32_t raw[8];
-  // rows past the bucket carry an offset beyond the buffer: the loads read zeros
+  static constexpr int kDw = 64 * BM / 256 / 2;  // dwords per thread: 8 (BM 64) or 2 (BM 16)
+  uint32_t raw[kDw];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int k) {
     const uint32_t vo = row_off + (uint32_t)k * 2u;
-    const u32x4_t q0 = buf_u128(r, vo, 0), q1 = buf_u128(r, vo + 16, 0);
-    raw[0] = q0.x, raw[1] = q0.y, raw[2] = q0.z, raw[3] = q0.w;
-    raw[4] = q1.x, raw[5] = q1.y, raw[6] = q1.z, raw[7] = q1.w;
+    if constexpr (kDw == 8) {
+      const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+      raw[0] = a.x, raw[1] = a.y, raw[2] = a.z, raw[3] = a.w;
+      raw[4] = b.x, raw[5] = b.y, raw[6] = b.z, raw[7] = b.w;
+    } else {
+      const u32x2_t a = buf_u64(r, vo, 0);
+      raw[0] = a.x, raw[1] = a.y;
+    }
   }
   __device__ __forceinline__ void store(uint32_t *dst) const {
-    uint32_t o[8];
+    uint32_t o[kDw];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < kDw; i++)
       o[i] = (MODE == kModeGateUp && OP == kOpF16) ? bf16x2_to_f16x2(raw[i]) : raw[i];
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-    d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    if constexpr (kDw == 8) {
+      uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+      d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
+    }
   }
 };
 
+// the bf16 weight column a lane of k group g loads in stage it
+__device__ __forceinline__ int a_k_b16(int it, int g) { return 256 * (it >> 2) + 64 * g + 16 * (it & 3); }
+
 template <int OP>
-__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+__device__ __forceinline__ f32x4v_t mfma16(uint4 a, uint4 b, f32x4v_t c) {
   if constexpr (OP == kOpBF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// the grouped GEMM: grid.x = column tiles of the layer, grid.y = bucket tiles
+// the grouped GEMM: grid.x = column blocks of the layer, grid.y = bucket tiles
 // ---------------------------------------------------------------------------
-template <int MODE, int FMT, int OP>
+template <int MODE, int FMT, int OP, int BM>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
-  __shared__ uint32_t s_a[2][kBM * kLdsW];
-  __shared__ uint32_t s_b[2][kBN * kLdsW];
-  __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 : 1];
-  // XCD-aware order: workgroups go round-robin to the 8 XCDs, so linear id b
-  // runs on XCD b % 8.  Give XCD x the tiles x, x + 8, ... and walk all column
-  // blocks of one tile back to back there, so its L2 fetches each A tile once.
+  constexpr int MB = BM / 16;  // MFMA row blocks
+  constexpr int kPA = 4;       // A stages in flight (one group)
+  constexpr bool kGroupB = FMT != MOE_FMT_BF16;
+  __shared__ uint32_t s_a[2][BM * kLdsRowW];
+  __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
+  // XCD-aware order: workgroups go round-robin to the 8 XCDs (linear id b on
+  // XCD b % 8); XCD x takes tiles x, x + 8, ... and walks all column blocks of
+  // a tile back to back, so its L2 fetches each tile's rows once.
   // (grid.y is a multiple of 8.)
   const uint32_t nbx = gridDim.x;
-  const uint32_t b = blockIdx.y * nbx + blockIdx.x;
-  const uint32_t j = b >> 3;
-  const int ti = (int)((j / nbx) * 8 + (b & 7));
-  const int bx = (int)(j % nbx);
+  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t jx = bid >> 3;
+  const int ti = (int)((jx / nbx) * 8 + (bid & 7));
+  const int bx = (int)(jx % nbx);
   if (ti >= p.tiles[0]) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
   const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  constexpr int kCols = MODE == kModeGateUp ? kBN / 2 : kBN;  // output columns per tile
+  const int lr = lane & 15, lg = lane >> 4;  // MFMA row/column within a block; k group
+  // output columns of this block: gate/up 128 (a columns), down 256
+  constexpr int kCols = MODE == kModeGateUp ? kWRows / 2 : kWRows;
   const int n0 = bx * kCols;
 
-  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook entries as exact operand pairs
+  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, kNCopy copies
     const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[tid];
-    float v[4];
+    uint32_t h[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = (float)(int)(int8_t)((cw >> (8 * j)) & 255u);
-    s_cb[tid] = make_uint2(pack2<OP>(v[0], v[1]), pack2<OP>(v[2], v[3]));
+    for (int j = 0; j < 2; j++)
+      h[j] = pack_h2((float)(int)(int8_t)((cw >> (16 * j)) & 255u),
+                     (float)(int)(int8_t)((cw >> (16 * j + 8)) & 255u));
+#pragma unroll
+    for (int c = 0; c < kNCopy; c++) s_cb[tid * kNCopy + c] = make_uint2(h[0], h[1]);
   }
 
-  // A staging: bucket row tid / 4
-  const int arow = tid >> 2, ak = (tid & 3) * 16;
+  // A staging: row tid / (256 / BM), LDS columns acol .. acol + kCPT - 1, which
+  // in stage it hold k = 256 (it / 4) + 64 (acol / 16) + 16 (it % 4) + acol % 16 + ...
+  constexpr int kTPR = kGemmThreads / BM;  // threads per A row
+  constexpr int kCPT = kBKs / kTPR;        // columns per thread
+  const int arow = tid / kTPR, acol = (tid % kTPR) * kCPT;
+  const int acol_k = 64 * (acol / 16) + acol % 16;
   const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)p.K * 2u;
   uint32_t a_off = a_bytes;  // past the end: zeros
   if (r0 + arow < r1) {
@@ -267,125 +331,120 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     a_off = (uint32_t)src * (uint32_t)p.K * 2u;
   }
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(MODE == kModeGateUp ? p.x : p.a16, a_bytes);
-  // B staging: tile row tid / 2 (waves 2, 3 stage the up rows of a gate/up tile)
-  const int brow = tid >> 1, bk = (tid & 1) * 32;
-  const bool b_up = MODE == kModeGateUp && wave >= 2;
-  const WView &bw = b_up ? p.w1 : p.w0;
-  const int wrow = MODE == kModeGateUp ? n0 + (brow & (kBN / 2 - 1)) : n0 + brow;
+  const int nk = p.K / kBKs;  // stages, a multiple of 4 (K % 256 == 0)
+  const int ng = nk / 4;      // groups
+  auto a_k = [&](int it) { return 256 * (it >> 2) + 16 * (it & 3) + acol_k; };
 
-  // kPD stages in flight: stage s is staged in registers slot s % kPD from the
-  // time its loads are issued until it is decoded into LDS, kPD - 1 stages
-  // before the MFMAs read it, which covers the HBM latency
-  constexpr int kPD = 4;
-  AStage<MODE, OP> sa[kPD];
-  BStage<FMT, OP> sb[kPD];
-  const int nk = p.K / kBK;
+  // this lane's four weight rows (column blocks nb = 0..3)
+  int wrow[4];
+  const WView *wv[4];
 #pragma unroll
-  for (int u = 0; u < kPD; u++) {  // nk >= kPD (K >= 256)
-    sa[u].load(ra, a_off, u * kBK + ak);
-    sb[u].load(bw, e, wrow, u * kBK + bk);
-  }
-  if constexpr (FMT == MOE_FMT_VQ2) __syncthreads();
-  sa[0].store(&s_a[0][arow * kLdsW + ak / 2]);
-  sb[0].store(&s_b[0][brow * kLdsW + bk / 2], s_cb);
-  {  // stages past the end re-read the last one (never used; keeps the loads unconditional)
-    const int st = min(kPD, nk - 1);
-    sa[0].load(ra, a_off, st * kBK + ak);
-    sb[0].load(bw, e, wrow, st * kBK + bk);
-  }
-  __syncthreads();
-
-  // the lane's two B columns: gate/up -> (gate, up) of column n0 + 32 wn + lane % 32;
-  // down -> columns n0 + 64 wn + lane % 32 and that + 32
-  const int cl = lane & 31;
-  const int bc0 = MODE == kModeGateUp ? 32 * wn + cl : 64 * wn + cl;
-  const int bc1 = MODE == kModeGateUp ? kBN / 2 + 32 * wn + cl : 64 * wn + 32 + cl;
-  const int arow_frag = 32 * wm + cl;
-  const int kh = 8 * (lane >> 5);
-  // a wave whose 32 rows all lie past the bucket's end skips its MFMAs
-  const bool active = r0 + 32 * wm < r1;
-
-  constexpr bool kGroupScale = FMT == MOE_FMT_VQ2;
-  // VQ2: the fp16 scales of the lane's two weight rows, all K / 256 <= 16 groups
-  uint32_t gsc0[kGroupScale ? 8 : 1] = {}, gsc1[kGroupScale ? 8 : 1] = {};
-  if constexpr (kGroupScale) {
-    const int wr0 = n0 + (MODE == kModeGateUp ? 32 * wn + cl : 64 * wn + cl);
-    const int wr1 = MODE == kModeGateUp ? wr0 : wr0 + 32;
-    const WView &v1 = MODE == kModeGateUp ? p.w1 : p.w0;
-    const uint32_t sbb = (uint32_t)expert_scale_bytes(FMT, p.w0.N, p.w0.K);
-    const uint32_t rb = (uint32_t)(p.K / 256) * 2u;  // scale bytes per row
-    const __amdgpu_buffer_rsrc_t s0 = make_rsrc(p.w0.scales + (size_t)e * sbb, sbb);
-    const __amdgpu_buffer_rsrc_t s1 = make_rsrc(v1.scales + (size_t)e * sbb, sbb);
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      // past the row's K / 256 groups this reads the next row (or zeros past
-      // the expert): never used, and it keeps the loads unconditional
-      gsc0[q] = buf_u32(s0, (uint32_t)wr0 * rb + 4 * q, 0);
-      gsc1[q] = buf_u32(s1, (uint32_t)wr1 * rb + 4 * q, 0);
+  for (int nb = 0; nb < 4; nb++) {
+    if constexpr (MODE == kModeGateUp) {  // nb 0, 1: gate; nb 2, 3: up; same 32 a columns
+      wrow[nb] = n0 + 32 * wave + 16 * (nb & 1) + lr;
+      wv[nb] = nb < 2 ? &p.w0 : &p.w1;
+    } else {
+      wrow[nb] = n0 + kWRowsPerWave * wave + 16 * nb + lr;
+      wv[nb] = &p.w0;
     }
   }
-  f32x16_t acc0 = {}, acc1 = {}, part0 = {}, part1 = {};
-  for (int it0 = 0; it0 < nk; it0 += kPD) {
+
+  AStage<MODE, OP, BM> sa[kPA];
+  BGroup<FMT, OP> gb0[4], gb1[4];    // group ring (quantized formats)
+  BStageBf16<OP> sb16[2][4];         // stage ring (bf16): two stages ahead
 #pragma unroll
-    for (int u = 0; u < kPD; u++) {
-      const int it = it0 + u;  // nk % kPD == 0 (K % 256 == 0)
+  for (int u = 0; u < kPA; u++) sa[u].load(ra, a_off, a_k(u));
+  if constexpr (kGroupB) {
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) gb0[nb].load(*wv[nb], e, wrow[nb], 64 * lg);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], a_k_b16(u, lg));
+  }
+  sa[0].store(&s_a[0][arow * kLdsRowW + acol / 2]);
+  // stages past the end re-read the last one (never used; keeps the loads unconditional)
+  sa[0].load(ra, a_off, a_k(min(kPA, nk - 1)));
+  __syncthreads();  // A stage 0 and the codebook
+
+  const int m_active = (r1 - r0 + 15) >> 4;  // row blocks holding bucket rows
+  f32x4v_t acc[MB][4];
+#pragma unroll
+  for (int m = 0; m < MB; m++)
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) acc[m][nb] = (f32x4v_t){0.0f, 0.0f, 0.0f, 0.0f};
+  const uint2 *cb = s_cb + (lane & (kNCopy - 1));
+
+  // one group: 4 stages; its B comes from `cur`, the next group's goes to `nxt`
+  auto group = [&](int G, BGroup<FMT, OP>(&cur)[4], BGroup<FMT, OP>(&nxt)[4]) {
+    if constexpr (kGroupB) {
+      const int gn = min(G + 1, ng - 1);
+#pragma unroll
+      for (int nb = 0; nb < 4; nb++) nxt[nb].load(*wv[nb], e, wrow[nb], 256 * gn + 64 * lg);
+    }
+#pragma unroll
+    for (int S = 0; S < 4; S++) {
+      const int it = 4 * G + S;
+      uint32_t bp[4][8];
+      if constexpr (kGroupB) {
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) cur[nb].decode(S, bp[nb], cb);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) sb16[S & 1][nb].decode(bp[nb]);
+        const int st = min(it + 2, nk - 1);
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], a_k_b16(st, lg));
+      }
       const uint32_t *A = s_a[it & 1];
-      const uint32_t *B = s_b[it & 1];
-      if (active) {
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ks++) {
-          const int kk = ks * 16 + kh;
-          const uint4 af = *reinterpret_cast<const uint4 *>(&A[arow_frag * kLdsW + kk / 2]);
-          const uint4 bf0 = *reinterpret_cast<const uint4 *>(&B[bc0 * kLdsW + kk / 2]);
-          const uint4 bf1 = *reinterpret_cast<const uint4 *>(&B[bc1 * kLdsW + kk / 2]);
-          if constexpr (kGroupScale) {
-            part0 = mfma32<OP>(af, bf0, part0);
-            part1 = mfma32<OP>(af, bf1, part1);
-          } else {
-            acc0 = mfma32<OP>(af, bf0, acc0);
-            acc1 = mfma32<OP>(af, bf1, acc1);
-          }
-        }
-        if constexpr (kGroupScale) {
-          if ((it + 1) % (256 / kBK) == 0) {  // a 256-column group is complete: scale and fold
-            const int kb = it / (256 / kBK);
-            const uint32_t h0 = gsc0[kb >> 1], h1 = gsc1[kb >> 1];
-            const float d0 = f16_bits_to_f32((kb & 1) ? h0 >> 16 : h0 & 0xFFFFu);
-            const float d1 = f16_bits_to_f32((kb & 1) ? h1 >> 16 : h1 & 0xFFFFu);
+      for (int t = 0; t < 2; t++) {
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-              acc0[i] = fmaf(d0, part0[i], acc0[i]);
-              acc1[i] = fmaf(d1, part1[i], acc1[i]);
-              part0[i] = 0.0f;
-              part1[i] = 0.0f;
-            }
+        for (int m = 0; m < MB; m++) {
+          if (MB > 1 && m >= m_active) continue;
+          const uint4 af =
+              *reinterpret_cast<const uint4 *>(&A[(16 * m + lr) * kLdsRowW + (16 * lg + 8 * t) / 2]);
+#pragma unroll
+          for (int nb = 0; nb < 4; nb++) {
+            const uint4 bf = make_uint4(bp[nb][4 * t], bp[nb][4 * t + 1], bp[nb][4 * t + 2],
+                                        bp[nb][4 * t + 3]);
+            acc[m][nb] = mfma16<OP>(af, bf, acc[m][nb]);
           }
         }
       }
-      // decode stage it + 1 into the other buffer, then refill its slot
-      const int slot = (u + 1) % kPD;
-      // (after the last stage this fills the idle buffer with a repeat: unread)
-      sa[slot].store(&s_a[(it + 1) & 1][arow * kLdsW + ak / 2]);
-      sb[slot].store(&s_b[(it + 1) & 1][brow * kLdsW + bk / 2], s_cb);
-      const int st = min(it + 1 + kPD, nk - 1);
-      sa[slot].load(ra, a_off, st * kBK + ak);
-      sb[slot].load(bw, e, wrow, st * kBK + bk);
+      // A: stage it + 1 into the other buffer, refill its slot
+      const int an = (S + 1) & 3;
+      sa[an].store(&s_a[(it + 1) & 1][arow * kLdsRowW + acol / 2]);
+      sa[an].load(ra, a_off, a_k(min(it + 1 + kPA, nk - 1)));
       __syncthreads();
     }
+  };
+  for (int G = 0; G < ng; G += 2) {
+    group(G, gb0, gb1);
+    if (G + 1 < ng) group(G + 1, gb1, gb0);
   }
 
-  // result i of the lane: tile row 32 wm + (i % 4) + 8 (i / 4) + 4 (lane / 32)
+  // result register i of the lane: row 16 m + 4 (lane / 16) + i, column lane % 16
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int r = r0 + 32 * wm + (i & 3) + 8 * (i >> 2) + 4 * (lane >> 5);
-    if (r >= r1) continue;
-    if constexpr (MODE == kModeGateUp) {
-      const float a = silu_mul(acc0[i], acc1[i]);
-      p.a_out[(size_t)r * p.N + n0 + 32 * wn + cl] = __builtin_bit_cast(uint16_t, (_Float16)a);
-    } else {
-      float *yr = p.y_out + (size_t)r * p.N + n0 + 64 * wn + cl;
-      yr[0] = acc0[i];
-      yr[32] = acc1[i];
+  for (int m = 0; m < MB; m++) {
+    if (m >= m_active) continue;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = r0 + 16 * m + 4 * lg + i;
+      if (r >= r1) continue;
+      if constexpr (MODE == kModeGateUp) {
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+          const float a = silu_mul(acc[m][c][i], acc[m][c + 2][i]);
+          p.a_out[(size_t)r * p.N + n0 + 32 * wave + 16 * c + lr] =
+              __builtin_bit_cast(uint16_t, (_Float16)a);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++)
+          p.y_out[(size_t)r * p.N + n0 + kWRowsPerWave * wave + 16 * nb + lr] = acc[m][nb][i];
+      }
     }
   }
 }
@@ -394,27 +453,24 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 // host
 // ---------------------------------------------------------------------------
 
-// K a multiple of 256 (whole Q2K / VQ2 groups; at least kPD stages); VQ2 keeps
-// all its K / 256 group scales of a row in registers: K <= 4096
+// K a multiple of 256 (whole Q2K / VQ2 groups; a whole number of register
+// stages), output columns a multiple of the block's (128 a columns, 256 down)
 bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
-  if (H < 256 || I < 256 || H % 256 || I % 256) return false;
-  if (fmt_gate == MOE_FMT_VQ2 && H > 4096) return false;
-  if (fmt_down == MOE_FMT_VQ2 && I > 4096) return false;
-  return true;
+  (void)fmt_gate, (void)fmt_down;
+  return H >= 256 && I >= 256 && H % 256 == 0 && I % 256 == 0;
 }
 
 namespace {
 
-template <int MODE>
+template <int MODE, int BM>
 hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s) {
-#define MOE_GEMM_CASE(F, O)                                \
-  if (fmt == F && op == O) {                               \
-    launch(k_gemm<MODE, F, O>, dim3(grid), dim3(kGemmThreads), s, a);   \
-    return hipGetLastError();                              \
+#define MOE_GEMM_CASE(F, O)                                           \
+  if (fmt == F && op == O) {                                          \
+    launch(k_gemm<MODE, F, O, BM>, grid, dim3(kGemmThreads), s, a);   \
+    return hipGetLastError();                                         \
   }
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpBF16)
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpF16)
-  MOE_GEMM_CASE(MOE_FMT_VQ2, kOpBF16)
   MOE_GEMM_CASE(MOE_FMT_VQ2, kOpF16)
   MOE_GEMM_CASE(MOE_FMT_Q2K, kOpF16)
   MOE_GEMM_CASE(MOE_FMT_MXFP4, kOpBF16)
@@ -423,18 +479,20 @@ hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-}  // namespace
+int gateup_op(int fmt) {
+  return fmt == MOE_FMT_VQ2 || fmt == MOE_FMT_Q2K ? kOpF16 : kOpBF16;
+}
 
-hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
-                           int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
-                           int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
-                           void (*mark)(void *, const char *), void *mark_ctx,
-                           const char *const names[3]) {
-  if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
+template <int BM>
+hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H, int I, int T,
+                   const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
+                   int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
+                   void (*mark)(void *, const char *), void *mark_ctx,
+                   const char *const names[3]) {
   const int E = offsets ? gate.E : 0;
-  const int max_tiles = ((n_rows + kBM - 1) / kBM + E + 7) / 8 * 8;
+  const int max_tiles = ((n_rows + BM - 1) / BM + E + 7) / 8 * 8;
   if (mark) mark(mark_ctx, names[0]);
-  launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, offsets, tiles);
+  launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, BM, offsets, tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -443,15 +501,32 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   g.row_token = offsets ? sorted_token : nullptr;
   g.tiles = tiles, g.a_out = a16;
   if (mark) mark(mark_ctx, names[1]);
-  err = gemm_fmt<kModeGateUp>(g, gate.fmt, gate.fmt == MOE_FMT_Q2K ? kOpF16 : kOpBF16,
-                              dim3(I / (kBN / 2), max_tiles), s);
+  err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt),
+                                  dim3(I / (kWRows / 2), max_tiles), s);
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
   d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.a16 = a16, d.a_rows = n_rows, d.tiles = tiles;
   d.y_out = y;
   if (mark) mark(mark_ctx, names[2]);
-  return gemm_fmt<kModeDown>(d, down.fmt, kOpF16, dim3(H / kBN, max_tiles), s);
+  return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, dim3(H / kWRows, max_tiles), s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
+                           int T, const uint16_t *x, const int32_t *offsets,
+                           const int32_t *sorted_token, int n_rows, int32_t *tiles, uint16_t *a16,
+                           float *y, hipStream_t s, void (*mark)(void *, const char *),
+                           void *mark_ctx, const char *const names[3]) {
+  if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
+  // rows per tile: 64 once the active experts average 32 rows or more, else 16
+  const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
+  if (n_rows >= 32 * active)
+    return gemm_bm<64>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y, s,
+                       mark, mark_ctx, names);
+  return gemm_bm<16>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y, s,
+                     mark, mark_ctx, names);
 }
 
 }  // namespace moe
