@@ -164,10 +164,13 @@ bool gemm_fits(int T, int H, int I, int n_rows) {
   return (size_t)T * H * 2 < lim && (size_t)n_rows * I * 2 < lim;
 }
 
-// the matrix cores pay once the buckets hold several rows each
+// The matrix-core path streams each expert's weights once for all its rows;
+// from a handful of tokens on it beats the per-token GEMV (one choice for
+// moe_expert_ffn and moe_forward alike, so the two compose exactly)
 bool use_gemm(int T, int H, int I, int E, int n_rows, bool dense, int fmt_gate, int fmt_down) {
+  (void)E;
   if (!gemm_supported(H, I, fmt_gate, fmt_down) || !gemm_fits(T, H, I, n_rows)) return false;
-  return dense ? n_rows >= 32 : (long long)n_rows >= 4LL * E;
+  return dense ? n_rows >= 32 : T >= 4;
 }
 
 int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView &u,
@@ -175,6 +178,10 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
             float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
   Marker none;
   Marker &m = mk ? *mk : none;
+  if (!offsets && skinny_supported(H, I, T, g, d))
+    return hip_check(launch_skinny_ffn(g, u, d, H, I, T, x, reinterpret_cast<uint16_t *>(b.a), y,
+                                       s, mark_cb, &m, kRoutedGemmNames),
+                     "skinny ffn");
   if (use_gemm(T, H, I, g.E, n_rows, !offsets, g.fmt, d.fmt))
     return hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
                                      reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m,
@@ -209,7 +216,7 @@ struct FwdBufs {
   float *a_sh, *shared_y;
   int32_t *tiles_sh;
   // small path
-  int32_t *plan, *sorted_token, *slot_pos;
+  int32_t *plan, *sorted_token, *slot_pos, *tiles;
   float *row_w, *a, *y_rows;
   // large path
   int32_t *offsets, *sorted_slot;
@@ -249,6 +256,8 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.row_w = c.take<float>(n);
     b.a = c.take<float>(n * I);
     b.y_rows = c.take<float>(n * H);
+    b.offsets = c.take<int32_t>(E + 1);
+    b.tiles = c.take<int32_t>(gemm_tile_ints((int)n, E));
   } else {
     b.offsets = c.take<int32_t>(E + 1);
     b.sorted_token = c.take<int32_t>(n);
@@ -462,7 +471,12 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
-    if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
+    if (skinny_supported(H, L->I_shared, T, sg, sd)) {
+      MOE_TRY(hip_check(launch_skinny_ffn(sg, su, sd, H, L->I_shared, T, x,
+                                          reinterpret_cast<uint16_t *>(b.a_sh), b.shared_y, s,
+                                          mark_cb, &mk, kSharedGemmNames),
+                        "shared skinny"));
+    } else if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
       MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
                                         b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh),
                                         b.shared_y, s, mark_cb, &mk, kSharedGemmNames),
@@ -480,15 +494,24 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
   const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
   if (fwd_small(L, T)) {
     mk("select_plan");
-    MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
+    MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, b.offsets,
                                     b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
                       "select"));
-    const int max_active = std::min(E, n);
-    mk("routed_gateup");
-    MOE_TRY(hip_check(
-        launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s), "gate/up"));
-    mk("routed_down");
-    MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
+    if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt)) {
+      // several tokens: every selected expert's weights once, all its rows per load
+      MOE_TRY(hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n,
+                                        b.tiles, reinterpret_cast<uint16_t *>(b.a), b.y_rows, s,
+                                        mark_cb, &mk, kRoutedGemmNames),
+                        "gemm ffn"));
+    } else {
+      const int max_active = std::min(E, n);
+      mk("routed_gateup");
+      MOE_TRY(hip_check(
+          launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s),
+          "gate/up"));
+      mk("routed_down");
+      MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
+    }
     mk("combine");
     return hip_check(
         launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),

@@ -450,6 +450,116 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// dense and skinny (one expert, T <= 64 rows, bf16 weights: the shared expert
+// of a small batch).  Block: 16 output columns; its 8 waves split K, each
+// streaming its share of the 16 (gate/up: 16 + 16) weight rows straight into
+// MFMA operands, A (the T rows) straight from global memory; the 8 partial
+// tiles are summed in wave order through LDS, then the SwiGLU / output.
+// ---------------------------------------------------------------------------
+constexpr int kSkWaves = 8;
+
+struct SkinnyArgs {
+  int T, K, N;
+  const uint16_t *w0, *w1;  // bf16 [N][K] (gate, up) or (down, -)
+  const uint16_t *a;        // gate/up: bf16 x [T][K]; down: fp16 SwiGLU output [T][K]
+  uint16_t *a_out;          // gate/up: fp16 [T][N]
+  float *y_out;             // down: fp32 [T][N]
+};
+
+template <int MODE, int MB>
+__global__ __launch_bounds__(64 * kSkWaves) void k_skinny(SkinnyArgs p) {
+  constexpr int NB = MODE == kModeGateUp ? 2 : 1;  // gate + up, or down
+  constexpr int OP = MODE == kModeGateUp ? kOpBF16 : kOpF16;
+  constexpr int kPD = MB > 2 ? 2 : 4;              // stages in flight
+  __shared__ f32x4v_t s_red[kSkWaves][MB][NB][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int c0 = blockIdx.x * 16;
+  const int ns = p.K / kBKs, per = ns / kSkWaves, st0 = wave * per;  // ns % 8 == 0
+  const uint32_t wbytes = (uint32_t)p.N * (uint32_t)p.K * 2u;
+  const __amdgpu_buffer_rsrc_t rw0 = make_rsrc(p.w0, wbytes);
+  const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(NB == 2 ? p.w1 : p.w0, wbytes);
+  const uint32_t abytes = (uint32_t)p.T * (uint32_t)p.K * 2u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, abytes);
+  const uint32_t wo = ((uint32_t)(c0 + lr) * (uint32_t)p.K + 16u * lg) * 2u;
+  uint32_t ao[MB];
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    const int t = 16 * m + lr;
+    ao[m] = t < p.T ? ((uint32_t)t * (uint32_t)p.K + 16u * lg) * 2u : abytes;  // past T: zeros
+  }
+  u32x4_t bw[kPD][NB][2], av[kPD][MB][2];
+  auto load = [&](int slot, int st) {
+    const uint32_t ko = (uint32_t)st * kBKs * 2u;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      bw[slot][0][h] = buf_u128(rw0, wo + ko + 16 * h, 0);
+      if constexpr (NB == 2) bw[slot][1][h] = buf_u128(rw1, wo + ko + 16 * h, 0);
+#pragma unroll
+      for (int m = 0; m < MB; m++) av[slot][m][h] = buf_u128(ra, ao[m] + ko + 16 * h, 0);
+    }
+  };
+  f32x4v_t acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; m++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[m][nb] = (f32x4v_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < kPD; u++) load(u, st0 + min(u, per - 1));
+  for (int i0 = 0; i0 < per; i0 += kPD) {
+#pragma unroll
+    for (int u = 0; u < kPD; u++) {
+      if (i0 + u < per) {
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++) {
+            const u32x4_t w = bw[u][nb][t];
+            const uint4 bf = OP == kOpF16
+                                 ? make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y),
+                                              bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w))
+                                 : make_uint4(w.x, w.y, w.z, w.w);
+#pragma unroll
+            for (int m = 0; m < MB; m++) {
+              const u32x4_t x = av[u][m][t];
+              acc[m][nb] = mfma16<OP>(make_uint4(x.x, x.y, x.z, x.w), bf, acc[m][nb]);
+            }
+          }
+        }
+        load(u, st0 + min(i0 + u + kPD, per - 1));
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MB; m++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) s_red[wave][m][nb][lane] = acc[m][nb];
+  __syncthreads();
+  if (wave != 0) return;
+  // result register i of the lane: row 16 m + 4 (lane / 16) + i, column c0 + lane % 16
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    f32x4v_t v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      v[nb] = s_red[0][m][nb][lane];
+#pragma unroll
+      for (int w = 1; w < kSkWaves; w++) v[nb] += s_red[w][m][nb][lane];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int t = 16 * m + 4 * lg + i;
+      if (t >= p.T) continue;
+      if constexpr (MODE == kModeGateUp)
+        p.a_out[(size_t)t * p.N + c0 + lr] = __builtin_bit_cast(uint16_t, (_Float16)silu_mul(v[0][i], v[1][i]));
+      else
+        p.y_out[(size_t)t * p.N + c0 + lr] = v[0][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
 
@@ -513,6 +623,38 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
 }
 
 }  // namespace
+
+template <int MB>
+static hipError_t skinny_mb(const WView &gate, const WView &up, const WView &down, int H, int I,
+                            int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
+                            void (*mark)(void *, const char *), void *mark_ctx,
+                            const char *const names[3]) {
+  SkinnyArgs g{T, H, I, reinterpret_cast<const uint16_t *>(gate.data),
+               reinterpret_cast<const uint16_t *>(up.data), x, a16, nullptr};
+  if (mark) mark(mark_ctx, names[1]);
+  launch(k_skinny<kModeGateUp, MB>, dim3(I / 16), dim3(64 * kSkWaves), s, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  SkinnyArgs d{T, I, H, reinterpret_cast<const uint16_t *>(down.data), nullptr, a16, nullptr, y};
+  if (mark) mark(mark_ctx, names[2]);
+  launch(k_skinny<kModeDown, MB>, dim3(H / 16), dim3(64 * kSkWaves), s, d);
+  return hipGetLastError();
+}
+
+bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down) {
+  return gate.fmt == MOE_FMT_BF16 && down.fmt == MOE_FMT_BF16 && gate.E == 1 && T >= 1 &&
+         T <= 64 && H % (kBKs * kSkWaves) == 0 && I % (kBKs * kSkWaves) == 0;
+}
+
+hipError_t launch_skinny_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
+                             int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
+                             void (*mark)(void *, const char *), void *mark_ctx,
+                             const char *const names[3]) {
+  if (!skinny_supported(H, I, T, gate, down)) return hipErrorInvalidValue;
+  if (T <= 16) return skinny_mb<1>(gate, up, down, H, I, T, x, a16, y, s, mark, mark_ctx, names);
+  if (T <= 32) return skinny_mb<2>(gate, up, down, H, I, T, x, a16, y, s, mark, mark_ctx, names);
+  return skinny_mb<4>(gate, up, down, H, I, T, x, a16, y, s, mark, mark_ctx, names);
+}
 
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                            int T, const uint16_t *x, const int32_t *offsets,

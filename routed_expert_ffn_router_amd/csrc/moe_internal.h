@@ -120,6 +120,14 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
                            void (*mark)(void *, const char *), void *mark_ctx,
                            const char *const names[3]);
 
+// dense one-expert FFN of T <= 64 rows with bf16 weights (a small batch's
+// shared expert): a16 fp16 [T][I], y fp32 [T][H]
+bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down);
+hipError_t launch_skinny_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
+                             int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
+                             void (*mark)(void *, const char *), void *mark_ctx,
+                             const char *const names[3]);
+
 // fused batch-1 decode (decode.hip) ------------------------------------------
 struct DecodeArgs {
   int H, I, E, k, Is, mode;
