@@ -35,12 +35,18 @@ constexpr int kBKs = 64;                  // K per stage
 constexpr int kLdsRow = kBKs + 8;         // padded LDS row (16-bit elements): 144 bytes
 constexpr int kLdsRowW = kLdsRow / 2;     // ... in dwords
 constexpr int kGemmThreads = 256;
-constexpr int kWRowsPerWave = 64;         // weight rows per wave (4 MFMA column blocks)
-constexpr int kWRows = 4 * kWRowsPerWave; // per block
+// MFMA column blocks (16 weight rows each) per wave
+template <int FMT>
+constexpr int col_blocks() { return 4; }
+
 constexpr int kMinBM = 16;
 
 enum { kOpBF16 = 0, kOpF16 = 1 };
 enum { kModeGateUp = 0, kModeDown = 1 };
+
+// output columns of one block (4 waves): gate/up a columns, down outputs
+template <int MODE, int FMT>
+constexpr int block_cols() { return MODE == kModeGateUp ? 32 * col_blocks<FMT>() : 64 * col_blocks<FMT>(); }
 
 // tile list: tiles[0] = count; tile i = tiles[1 + 3i .. 3 + 3i] = {expert, r0, r1}
 size_t gemm_tile_ints(int n_rows, int E) {
@@ -100,6 +106,7 @@ struct GemmArgs {
   const uint16_t *a16;       // down: fp16 SwiGLU output [n_rows][K]
   int a_rows;                // rows of x (gate/up: T) or of a16 (down: n_rows)
   const int32_t *tiles;
+  int weight_major;          // tile order: weights-first (one dense expert) or rows-first
   uint16_t *a_out;           // gate/up: fp16 [n_rows][N]
   float *y_out;              // down: fp32 [n_rows][N]
 };
@@ -231,22 +238,28 @@ struct BStageBf16 {
   }
 };
 
-// A stage: BM rows x 64 columns; thread t stages row t / (256 / BM), a run of
-// 64 * BM / 256 columns; rows past the bucket read zeros (an offset past the
-// buffer)
+// A stage: BM rows x 64 LDS columns; thread t stages row t / (256 / BM) and
+// the BM / 4 LDS columns from acol.  LDS column c of stage it holds
+// k = kb(it) + 64 (c / 16) + c % 16 with kb(it) = 256 (it / 4) + 16 (it % 4),
+// so a thread's columns are one run of 4 (BM 16) or runs of 16 (BM 64, 128)
+// 64 apart in k.  Rows past the bucket read zeros (an offset past the buffer).
 template <int MODE, int OP, int BM>
 struct AStage {
-  static constexpr int kDw = 64 * BM / 256 / 2;  // dwords per thread: 8 (BM 64) or 2 (BM 16)
+  static constexpr int kCPT = BM / 4;   // columns per thread
+  static constexpr int kDw = kCPT / 2;  // dwords per thread: 2, 8 or 16
   uint32_t raw[kDw];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int k) {
-    const uint32_t vo = row_off + (uint32_t)k * 2u;
-    if constexpr (kDw == 8) {
-      const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
-      raw[0] = a.x, raw[1] = a.y, raw[2] = a.z, raw[3] = a.w;
-      raw[4] = b.x, raw[5] = b.y, raw[6] = b.z, raw[7] = b.w;
-    } else {
-      const u32x2_t a = buf_u64(r, vo, 0);
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int kb, int acol) {
+    if constexpr (kCPT == 4) {
+      const u32x2_t a = buf_u64(r, row_off + (uint32_t)(kb + 64 * (acol / 16) + acol % 16) * 2u, 0);
       raw[0] = a.x, raw[1] = a.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < kCPT / 16; q++) {
+        const uint32_t vo = row_off + (uint32_t)(kb + 64 * (acol / 16 + q)) * 2u;
+        const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+        raw[8 * q] = a.x, raw[8 * q + 1] = a.y, raw[8 * q + 2] = a.z, raw[8 * q + 3] = a.w;
+        raw[8 * q + 4] = b.x, raw[8 * q + 5] = b.y, raw[8 * q + 6] = b.z, raw[8 * q + 7] = b.w;
+      }
     }
   }
   __device__ __forceinline__ void store(uint32_t *dst) const {
@@ -254,12 +267,12 @@ struct AStage {
 #pragma unroll
     for (int i = 0; i < kDw; i++)
       o[i] = (MODE == kModeGateUp && OP == kOpF16) ? bf16x2_to_f16x2(raw[i]) : raw[i];
-    if constexpr (kDw == 8) {
-      uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-      d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    } else {
+    if constexpr (kDw == 2) {
       *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
+    } else {
+      uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+      for (int i = 0; i < kDw / 4; i++) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
     }
   }
 };
@@ -283,19 +296,23 @@ __device__ __forceinline__ f32x4v_t mfma16(uint4 a, uint4 b, f32x4v_t c) {
 template <int MODE, int FMT, int OP, int BM>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr int MB = BM / 16;  // MFMA row blocks
+  constexpr int NB = col_blocks<FMT>();
   constexpr int kPA = 4;       // A stages in flight (one group)
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
   __shared__ uint32_t s_a[2][BM * kLdsRowW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   // XCD-aware order: workgroups go round-robin to the 8 XCDs (linear id b on
-  // XCD b % 8); XCD x takes tiles x, x + 8, ... and walks all column blocks of
-  // a tile back to back, so its L2 fetches each tile's rows once.
-  // (grid.y is a multiple of 8.)
-  const uint32_t nbx = gridDim.x;
+  // XCD b % 8).  Grouped experts (a tile or two each): XCD x takes tiles x,
+  // x + 8, ... and walks all column blocks of a tile back to back, so its L2
+  // fetches each tile's rows once.  One dense expert over many tiles: XCD x
+  // takes column blocks x, x + 8, ... and walks all tiles of one back to back,
+  // so its L2 keeps that block of weights.  (grid.y, and grid.x in the dense
+  // order, are multiples of 8.)
+  const uint32_t nbx = gridDim.x, nby = gridDim.y;
   const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
   const uint32_t jx = bid >> 3;
-  const int ti = (int)((jx / nbx) * 8 + (bid & 7));
-  const int bx = (int)(jx % nbx);
+  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
+  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
   if (ti >= p.tiles[0]) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
@@ -303,9 +320,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;  // MFMA row/column within a block; k group
-  // output columns of this block: gate/up 128 (a columns), down 256
-  constexpr int kCols = MODE == kModeGateUp ? kWRows / 2 : kWRows;
-  const int n0 = bx * kCols;
+  const int n0 = bx * block_cols<MODE, FMT>();
 
   if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, kNCopy copies
     const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[tid];
@@ -318,12 +333,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     for (int c = 0; c < kNCopy; c++) s_cb[tid * kNCopy + c] = make_uint2(h[0], h[1]);
   }
 
-  // A staging: row tid / (256 / BM), LDS columns acol .. acol + kCPT - 1, which
-  // in stage it hold k = 256 (it / 4) + 64 (acol / 16) + 16 (it % 4) + acol % 16 + ...
+  // A staging: row tid / (256 / BM), LDS columns acol .. acol + BM / 4 - 1
   constexpr int kTPR = kGemmThreads / BM;  // threads per A row
   constexpr int kCPT = kBKs / kTPR;        // columns per thread
   const int arow = tid / kTPR, acol = (tid % kTPR) * kCPT;
-  const int acol_k = 64 * (acol / 16) + acol % 16;
   const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)p.K * 2u;
   uint32_t a_off = a_bytes;  // past the end: zeros
   if (r0 + arow < r1) {
@@ -333,69 +346,71 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(MODE == kModeGateUp ? p.x : p.a16, a_bytes);
   const int nk = p.K / kBKs;  // stages, a multiple of 4 (K % 256 == 0)
   const int ng = nk / 4;      // groups
-  auto a_k = [&](int it) { return 256 * (it >> 2) + 16 * (it & 3) + acol_k; };
+  auto a_kb = [&](int it) { return 256 * (it >> 2) + 16 * (it & 3); };
 
-  // this lane's four weight rows (column blocks nb = 0..3)
-  int wrow[4];
-  const WView *wv[4];
+  // this lane's weight rows, one per column block nb: gate/up: the first half
+  // of the blocks gate rows, the second half the up rows of the same a columns
+  constexpr int kWaveCols = MODE == kModeGateUp ? 8 * NB : 16 * NB;  // output columns per wave
+  int wrow[NB];
+  const WView *wv[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; nb++) {
-    if constexpr (MODE == kModeGateUp) {  // nb 0, 1: gate; nb 2, 3: up; same 32 a columns
-      wrow[nb] = n0 + 32 * wave + 16 * (nb & 1) + lr;
-      wv[nb] = nb < 2 ? &p.w0 : &p.w1;
+  for (int nb = 0; nb < NB; nb++) {
+    if constexpr (MODE == kModeGateUp) {
+      wrow[nb] = n0 + kWaveCols * wave + 16 * (nb % (NB / 2)) + lr;
+      wv[nb] = nb < NB / 2 ? &p.w0 : &p.w1;
     } else {
-      wrow[nb] = n0 + kWRowsPerWave * wave + 16 * nb + lr;
+      wrow[nb] = n0 + kWaveCols * wave + 16 * nb + lr;
       wv[nb] = &p.w0;
     }
   }
 
   AStage<MODE, OP, BM> sa[kPA];
-  BGroup<FMT, OP> gb0[4], gb1[4];    // group ring (quantized formats)
-  BStageBf16<OP> sb16[2][4];         // stage ring (bf16): two stages ahead
+  BGroup<FMT, OP> gb0[NB], gb1[NB];  // group ring (quantized formats)
+  BStageBf16<OP> sb16[2][NB];        // stage ring (bf16): two stages ahead
 #pragma unroll
-  for (int u = 0; u < kPA; u++) sa[u].load(ra, a_off, a_k(u));
+  for (int u = 0; u < kPA; u++) sa[u].load(ra, a_off, a_kb(u), acol);
   if constexpr (kGroupB) {
 #pragma unroll
-    for (int nb = 0; nb < 4; nb++) gb0[nb].load(*wv[nb], e, wrow[nb], 64 * lg);
+    for (int nb = 0; nb < NB; nb++) gb0[nb].load(*wv[nb], e, wrow[nb], 64 * lg);
   } else {
 #pragma unroll
     for (int u = 0; u < 2; u++)
 #pragma unroll
-      for (int nb = 0; nb < 4; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], a_k_b16(u, lg));
+      for (int nb = 0; nb < NB; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], a_k_b16(u, lg));
   }
   sa[0].store(&s_a[0][arow * kLdsRowW + acol / 2]);
   // stages past the end re-read the last one (never used; keeps the loads unconditional)
-  sa[0].load(ra, a_off, a_k(min(kPA, nk - 1)));
+  sa[0].load(ra, a_off, a_kb(min(kPA, nk - 1)), acol);
   __syncthreads();  // A stage 0 and the codebook
 
   const int m_active = (r1 - r0 + 15) >> 4;  // row blocks holding bucket rows
-  f32x4v_t acc[MB][4];
+  f32x4v_t acc[MB][NB];
 #pragma unroll
   for (int m = 0; m < MB; m++)
 #pragma unroll
-    for (int nb = 0; nb < 4; nb++) acc[m][nb] = (f32x4v_t){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NB; nb++) acc[m][nb] = (f32x4v_t){0.0f, 0.0f, 0.0f, 0.0f};
   const uint2 *cb = s_cb + (lane & (kNCopy - 1));
 
   // one group: 4 stages; its B comes from `cur`, the next group's goes to `nxt`
-  auto group = [&](int G, BGroup<FMT, OP>(&cur)[4], BGroup<FMT, OP>(&nxt)[4]) {
+  auto group = [&](int G, BGroup<FMT, OP>(&cur)[NB], BGroup<FMT, OP>(&nxt)[NB]) {
     if constexpr (kGroupB) {
       const int gn = min(G + 1, ng - 1);
 #pragma unroll
-      for (int nb = 0; nb < 4; nb++) nxt[nb].load(*wv[nb], e, wrow[nb], 256 * gn + 64 * lg);
+      for (int nb = 0; nb < NB; nb++) nxt[nb].load(*wv[nb], e, wrow[nb], 256 * gn + 64 * lg);
     }
 #pragma unroll
     for (int S = 0; S < 4; S++) {
       const int it = 4 * G + S;
-      uint32_t bp[4][8];
+      uint32_t bp[NB][8];
       if constexpr (kGroupB) {
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) cur[nb].decode(S, bp[nb], cb);
+        for (int nb = 0; nb < NB; nb++) cur[nb].decode(S, bp[nb], cb);
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) sb16[S & 1][nb].decode(bp[nb]);
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[nb]);
         const int st = min(it + 2, nk - 1);
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], a_k_b16(st, lg));
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], a_k_b16(st, lg));
       }
       const uint32_t *A = s_a[it & 1];
 #pragma unroll
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
           const uint4 af =
               *reinterpret_cast<const uint4 *>(&A[(16 * m + lr) * kLdsRowW + (16 * lg + 8 * t) / 2]);
 #pragma unroll
-          for (int nb = 0; nb < 4; nb++) {
+          for (int nb = 0; nb < NB; nb++) {
             const uint4 bf = make_uint4(bp[nb][4 * t], bp[nb][4 * t + 1], bp[nb][4 * t + 2],
                                         bp[nb][4 * t + 3]);
             acc[m][nb] = mfma16<OP>(af, bf, acc[m][nb]);
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       // A: stage it + 1 into the other buffer, refill its slot
       const int an = (S + 1) & 3;
       sa[an].store(&s_a[(it + 1) & 1][arow * kLdsRowW + acol / 2]);
-      sa[an].load(ra, a_off, a_k(min(it + 1 + kPA, nk - 1)));
+      sa[an].load(ra, a_off, a_kb(min(it + 1 + kPA, nk - 1)), acol);
       __syncthreads();
     }
   };
@@ -435,15 +450,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       if (r >= r1) continue;
       if constexpr (MODE == kModeGateUp) {
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          const float a = silu_mul(acc[m][c][i], acc[m][c + 2][i]);
-          p.a_out[(size_t)r * p.N + n0 + 32 * wave + 16 * c + lr] =
+        for (int c = 0; c < NB / 2; c++) {
+          const float a = silu_mul(acc[m][c][i], acc[m][c + NB / 2][i]);
+          p.a_out[(size_t)r * p.N + n0 + kWaveCols * wave + 16 * c + lr] =
               __builtin_bit_cast(uint16_t, (_Float16)a);
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++)
-          p.y_out[(size_t)r * p.N + n0 + kWRowsPerWave * wave + 16 * nb + lr] = acc[m][nb][i];
+        for (int nb = 0; nb < NB; nb++)
+          p.y_out[(size_t)r * p.N + n0 + kWaveCols * wave + 16 * nb + lr] = acc[m][nb][i];
       }
     }
   }
@@ -572,12 +587,14 @@ bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
 
 namespace {
 
+// grid.x: the layer's output columns over the block's; grid.y: tiles
 template <int MODE, int BM>
-hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, dim3 grid, hipStream_t s) {
-#define MOE_GEMM_CASE(F, O)                                           \
-  if (fmt == F && op == O) {                                          \
-    launch(k_gemm<MODE, F, O, BM>, grid, dim3(kGemmThreads), s, a);   \
-    return hipGetLastError();                                         \
+hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s) {
+#define MOE_GEMM_CASE(F, O)                                                              \
+  if (fmt == F && op == O) {                                                             \
+    launch(k_gemm<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),             \
+           dim3(kGemmThreads), s, a);                                                    \
+    return hipGetLastError();                                                            \
   }
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpBF16)
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpF16)
@@ -610,16 +627,18 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x, g.a_rows = T;
   g.row_token = offsets ? sorted_token : nullptr;
   g.tiles = tiles, g.a_out = a16;
+  // one dense expert with many row tiles: keep each weight block in an L2
+  g.weight_major = !offsets && (I / block_cols<kModeGateUp, MOE_FMT_BF16>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
-  err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt),
-                                  dim3(I / (kWRows / 2), max_tiles), s);
+  err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s);
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
   d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.a16 = a16, d.a_rows = n_rows, d.tiles = tiles;
+  d.weight_major = !offsets && (H / block_cols<kModeDown, MOE_FMT_BF16>()) % 8 == 0 && max_tiles >= 16;
   d.y_out = y;
   if (mark) mark(mark_ctx, names[2]);
-  return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, dim3(H / kWRows, max_tiles), s);
+  return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, max_tiles, s);
 }
 
 }  // namespace
@@ -662,8 +681,12 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
                            float *y, hipStream_t s, void (*mark)(void *, const char *),
                            void *mark_ctx, const char *const names[3]) {
   if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
-  // rows per tile: 64 once the active experts average 32 rows or more, else 16
+  // rows per tile: 128 once the active experts average 96 rows or more (each
+  // weight read for more rows), 64 from 32 rows, else 16
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
+  if (n_rows >= 96 * active)
+    return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y,
+                        s, mark, mark_ctx, names);
   if (n_rows >= 32 * active)
     return gemm_bm<64>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y, s,
                        mark, mark_ctx, names);

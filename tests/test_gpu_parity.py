@@ -331,7 +331,7 @@ def _gemm_rows_case(layer, dl, dev, x, off, st, n_sample, seed):
     return normwise(y[rows], ref)
 
 
-@pytest.mark.parametrize("T", [128, 161])
+@pytest.mark.parametrize("T", [4, 16, 128, 161, 3072])
 def test_expert_ffn_gemm_q2(dev, q2, dq2, T):
     x = synth.gen_x(4096, T, seed=70 + T)
     idx, _, _ = oracle.LayerRef(q2).route(x)
@@ -358,7 +358,18 @@ def test_expert_ffn_gemm_ragged_buckets(dev, q2, dq2):
     assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 91) < TOL
 
 
-@pytest.mark.parametrize("T", [32, 97])
+def test_expert_ffn_gemm_ragged_buckets_128(dev, q2, dq2):
+    """Bucket sizes around the 128-row tile (enough rows for 128-row tiles)."""
+    sizes = np.array([0, 1, 127, 128, 129, 255, 256, 257, 95, 96, 97, 300] * 22)[:256]
+    assert sizes.sum() >= 96 * 256
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 97
+    st = np.random.default_rng(6).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=92)
+    assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 93) < TOL
+
+
+@pytest.mark.parametrize("T", [2, 16, 33, 64, 97, 1100])
 def test_expert_ffn_dense_shared_gemm(dev, q2, dq2, T):
     x = synth.gen_x(4096, T, seed=T)
     sg = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, dq2.shared_gate)
