@@ -39,7 +39,9 @@ struct Logits {
 
 // Lane j < k returns choice j in (*e_out, *w_out); other lanes get e = -1.
 // E <= 64 * NC; every lane of the wave must call this.  Softmax top-k reads
-// only the preloaded logits; hash routing reads the k selected ones.
+// only the preloaded logits (lg); hash routing takes the k selected ones from
+// lg too when E <= 64 * NC (from memory otherwise), so lg is loaded in both
+// modes.
 template <int NC>
 __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits<NC> &lg,
                                             const float *__restrict__ l, int64_t tid, int *e_out,
@@ -49,9 +51,22 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
   float my_l = -INFINITY;
   if (mode == MOE_ROUTE_HASH) {
     const uint64_t z = splitmix64((uint64_t)tid);
+    const int e = (int)((z + (uint64_t)lane) % (uint64_t)E);
+    float r;
+    if (E <= 64 * NC) {
+      // its logit from the preloaded ones: slot e / 64 of lane e % 64
+      r = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; i++) {
+        const float t = __shfl(lg.v[i], e & 63, 64);
+        if (i == (e >> 6)) r = t;
+      }
+    } else {
+      r = l[e];
+    }
     if (lane < k) {
-      my_e = (int)((z + (uint64_t)lane) % (uint64_t)E);
-      my_l = l[my_e];
+      my_e = e;
+      my_l = r;
     }
   } else {
     float v[NC];
@@ -113,11 +128,11 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const float 
                                             int64_t tid, int *e_out, float *w_out) {
   if (E <= 256) {
     Logits<4> lg;
-    if (mode != MOE_ROUTE_HASH) lg.load(E, l);
+    lg.load(E, l);
     select_wave<4>(mode, E, k, lg, l, tid, e_out, w_out);
   } else {
     Logits<kMaxE / 64> lg;
-    if (mode != MOE_ROUTE_HASH) lg.load(E, l);
+    lg.load(E, l);
     select_wave<kMaxE / 64>(mode, E, k, lg, l, tid, e_out, w_out);
   }
 }
