@@ -5,18 +5,18 @@
 // hysenlabs.com "SSD streaming"; matrix-instruction expert kernels on newer
 // devices -- hysenlabs.com "Model support and quantization").  Each workgroup
 // computes BM bucket rows of one expert against 256 weight rows (gate/up: 128
-// gate + 128 up; down: 256 outputs): BM = 64 for prefill, 16 for skinny
-// batches.  Each of the 4 waves owns 64 weight rows for all BM rows and
+// gate + 128 up; down: 256 outputs), BM in {16, 64, 128} by the rows per
+// active expert.  Each of the 4 waves owns 64 weight rows for all BM rows and
 // dequantizes them straight into MFMA operand registers -- every weight is
 // decoded once per tile and never passes through LDS; only the activation
 // rows (gathered tokens, or the SwiGLU output in bucket order) are staged in
 // LDS and shared by the waves.  v_mfma_f32_16x16x32 throughout.
 //
-// K is walked in stages of 64.  In stage s, lane l of a wave covers the 16
-// consecutive weights k = 64 s + 16 (l / 16) + [0, 16) of its row (the MFMA's
-// reduction slots are a relabelling of k; A and B use the same one), so a
-// lane decodes exactly one Q2K sub-block, four VQ2 codes or eight MXFP4 bytes
-// per row and stage.
+// K is walked in groups of 256 (one Q2K super-block, one VQ2 scale group),
+// each cut into 4 stages of 64: a lane loads its weights once per group (the
+// contiguous run of 64 it covers over the group's stages, see BGroup) and
+// decodes one stage ahead of the matrix instructions that consume it.  The
+// MFMA reduction slots are a relabelling of k; A and B use the same one.
 //
 // Operand precision: bf16 tokens x exact bf16 weights for MXFP4 and bf16
 // gate/up; fp16 for VQ2 and Q2K gate/up (tokens converted exactly, weights
@@ -391,6 +391,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     for (int nb = 0; nb < NB; nb++) acc[m][nb] = (f32x4v_t){0.0f, 0.0f, 0.0f, 0.0f};
   const uint2 *cb = s_cb + (lane & (kNCopy - 1));
 
+  // B operands of two stages: the MFMAs of stage `it` read bp[it & 1] while
+  // stage it + 1 is decoded into the other slot, so the decode's LDS lookups
+  // and VALU work overlap the matrix instructions instead of preceding them
+  uint32_t bp[2][NB][8];
+  if constexpr (kGroupB) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) gb0[nb].decode(0, bp[0][nb], cb);
+  }
+
   // one group: 4 stages; its B comes from `cur`, the next group's goes to `nxt`
   auto group = [&](int G, BGroup<FMT, OP>(&cur)[NB], BGroup<FMT, OP>(&nxt)[NB]) {
     if constexpr (kGroupB) {
@@ -401,30 +410,42 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int S = 0; S < 4; S++) {
       const int it = 4 * G + S;
-      uint32_t bp[NB][8];
-      if constexpr (kGroupB) {
+      // this stage's A fragments, all read before the matrix instructions
+      const uint32_t *A = s_a[it & 1];
+      uint4 af[2][MB];
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++) cur[nb].decode(S, bp[nb], cb);
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int m = 0; m < MB; m++)
+          af[t][m] =
+              *reinterpret_cast<const uint4 *>(&A[(16 * m + lr) * kLdsRowW + (16 * lg + 8 * t) / 2]);
+      if constexpr (kGroupB) {
+        // the next stage: stage S + 1 of this group, or stage 0 of the next
+        // (past the last group: a decode of the clamped reload, never used)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          if (S < 3)
+            cur[nb].decode(S + 1, bp[(S + 1) & 1][nb], cb);
+          else
+            nxt[nb].decode(0, bp[(S + 1) & 1][nb], cb);
+        }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[nb]);
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[S & 1][nb]);
         const int st = min(it + 2, nk - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], a_k_b16(st, lg));
       }
-      const uint32_t *A = s_a[it & 1];
 #pragma unroll
       for (int t = 0; t < 2; t++) {
 #pragma unroll
         for (int m = 0; m < MB; m++) {
           if (MB > 1 && m >= m_active) continue;
-          const uint4 af =
-              *reinterpret_cast<const uint4 *>(&A[(16 * m + lr) * kLdsRowW + (16 * lg + 8 * t) / 2]);
 #pragma unroll
           for (int nb = 0; nb < NB; nb++) {
-            const uint4 bf = make_uint4(bp[nb][4 * t], bp[nb][4 * t + 1], bp[nb][4 * t + 2],
-                                        bp[nb][4 * t + 3]);
-            acc[m][nb] = mfma16<OP>(af, bf, acc[m][nb]);
+            const uint32_t *b = bp[S & 1][nb];
+            const uint4 bf = make_uint4(b[4 * t], b[4 * t + 1], b[4 * t + 2], b[4 * t + 3]);
+            acc[m][nb] = mfma16<OP>(af[t][m], bf, acc[m][nb]);
           }
         }
       }
