@@ -73,15 +73,27 @@ KERNEL_OF = {"decode_p1": "k_dec_p1", "decode_p2": "k_dec_p2", "decode_p3": "k_d
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def sources_sha():
-    """Digest of every source the kernels are built from: counters recorded
-    against another digest describe other kernels and are not reported."""
+# kernel symbol substring -> the source file it is built from
+SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"),
+             ("k_skinny", "gemm.hip"), ("k_router", "route.hip"), ("k_select", "route.hip"),
+             ("k_chunk", "route.hip"), ("k_plan", "route.hip"), ("k_gateup", "gemv.hip"),
+             ("k_down", "gemv.hip"), ("k_dequant", "gemv.hip"), ("k_combine", "combine.hip"))
+
+
+def sources_sha(kernel):
+    """Digest of the sources kernel `kernel` (a symbol) is built from: its own
+    .hip file, every shared header and the ABI header.  Counters recorded
+    against another digest describe another kernel and are not reported."""
     import glob
     import hashlib
 
-    h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc", "*"))) + \
+    src = next((f for sub, f in SOURCE_OF if sub in kernel), None)
+    if src is None:
+        return None
+    csrc = os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc")
+    files = [os.path.join(csrc, src)] + sorted(glob.glob(os.path.join(csrc, "*.h"))) + \
         [os.path.join(ROOT, "include", "moe.h")]
+    h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -128,14 +140,14 @@ def pmc_summary(args):
         f_b = float(np.mean(fetch[k])) * 1024.0 * scale["fetch"]
         w_b = float(np.mean(write[k])) * 1024.0 * scale["write"]
         kernels[k] = {"fetch_bytes": f_b, "write_bytes": w_b, "bytes": f_b + w_b,
-                      "launches": len(fetch[k])}
+                      "launches": len(fetch[k]), "sources_sha": sources_sha(k)}
         lines.append(f"{k[:64]:64s} {len(fetch[k]):8d} {f_b / 1e6:10.3f} {w_b / 1e6:10.3f} "
                      f"{(f_b + w_b) / 1e6:10.3f}")
     db = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             db = json.load(fh)
-    db[args.workload] = {"sources_sha": sources_sha(), "scale": scale, "kernels": kernels}
+    db[args.workload] = {"scale": scale, "kernels": kernels}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(db, fh, indent=1, sort_keys=True)
     print("\n".join(lines))
@@ -148,10 +160,12 @@ def measured_traffic(workload, marker):
         return None
     with open(TRAFFIC_FILE) as fh:
         rec = json.load(fh).get(workload)
-    if not rec or rec.get("sources_sha") != sources_sha():
+    if not rec:
         return None
-    hits = [v["bytes"] for k, v in rec["kernels"].items() if KERNEL_OF[marker] in k]
-    return hits[0] if len(hits) == 1 else None
+    hits = [(k, v) for k, v in rec["kernels"].items() if KERNEL_OF[marker] in k]
+    if len(hits) != 1 or hits[0][1].get("sources_sha") != sources_sha(hits[0][0]):
+        return None
+    return hits[0][1]["bytes"]
 
 
 def copy_probe(mib):
