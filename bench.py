@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s; prefill tokens/s @2048"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense fp8 (an FP8 x FP4 product runs at the FP8 rate)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -69,12 +70,14 @@ KERNEL_OF = {"decode_p1": "k_dec_p1", "decode_p2": "k_dec_p2", "decode_p3": "k_d
              "router": "k_router", "gemm_gateup": "k_gemm<0, 2", "gemm_down": "k_gemm<1, 1",
              "combine": "k_combine", "select": "k_select", "select_plan": "k_select_plan",
              "routed_gateup": "k_gateup", "routed_down": "k_down", "shared_gateup": "k_gateup",
-             "shared_down": "k_down"}
+             "shared_down": "k_down", "a8_gemm_gateup": "k_gemm_a8<0", "a8_gemm_down": "k_gemm_a8<1",
+             "act_quant": "k_mx8_quant"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 # kernel symbol substring -> the source file it is built from
-SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"),
+SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm_a8", "gemm_fp4.hip"), ("k_mx8", "gemm_fp4.hip"),
+             ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"),
              ("k_skinny", "gemm.hip"), ("k_router", "route.hip"), ("k_select", "route.hip"),
              ("k_chunk", "route.hip"), ("k_plan", "route.hip"), ("k_gateup", "gemv.hip"),
              ("k_down", "gemv.hip"), ("k_dequant", "gemv.hip"), ("k_combine", "combine.hip"))
@@ -220,6 +223,10 @@ def kernel_cost(name, L, T, U, n):
         "down_gemv": (U * dn + n * I * 4 + n * H * 4, 2 * n * H * I),
         "gemm_gateup": (U * gu + cb + xb + n * I * 2, 4 * n * I * H),
         "gemm_down": (U * dn + n * I * 2 + n * H * 4, 2 * n * H * I),
+        # MX-FP8 activations (1 byte + a scale byte per 32) on the FP4 matrix cores
+        "act_quant": (xb + T * H + T * H // 32, 0),
+        "a8_gemm_gateup": (U * gu + T * H + T * H // 32 + n * I + n * I // 32, 4 * n * I * H),
+        "a8_gemm_down": (U * dn + n * I + n * I // 32 + n * H * 4, 2 * n * H * I),
         "combine": (n * H * 4 + 2 * T * H * 4 + n * 8, 2 * n * H),
     }
     return table.get(name, (0, 0))
@@ -251,7 +258,7 @@ def setup(wname, replicas, seed, npool, dev):
 
     w = synth.WORKLOADS[wname]
     host = synth.gen_layer(w.layer, seed)
-    base = moe.DeviceLayer.upload(host, route_mode=w.route, device=dev)
+    base = moe.DeviceLayer.upload(host, route_mode=w.route, device=dev, act=w.act)
     layers = [base] + [base.clone() for _ in range(replicas - 1)]
     xs, lgs, tids = [], [], []
     for i in range(npool):
@@ -404,11 +411,13 @@ def measure(wname, args, dev, headline):
     d = per[dom]
     # a launch whose flops per algorithmic byte exceed the chip's balance point
     # (2.5 PFLOP/s over 8 TB/s) is priced against the matrix cores
-    mfma = d["flops"] > (MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)) * d["bytes"]
+    # (the MX-FP8 x FP4 kernels against the FP8 matrix peak)
+    peak = MFMA_FP8_PEAK_TFLOPS if dom.startswith("a8_") else MFMA_PEAK_TFLOPS
+    mfma = d["flops"] > (peak * 1e12 / (HBM_PEAK_GBPS * 1e9)) * d["bytes"]
     if mfma:
         res["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"],
-                           "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": d["tflops"] / MFMA_PEAK_TFLOPS, "traffic": None,
+                           "peak": peak, "unit": "TFLOP/s",
+                           "frac": d["tflops"] / peak, "traffic": None,
                            "flops_per_launch": d["flops"], "us_per_launch": d["us"]}
     else:
         res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": d["gbps"],

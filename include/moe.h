@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum {
   MOE_OK = 0,
@@ -84,14 +84,30 @@ typedef struct {
   const int8_t *codebook;  /* VQ2: int8 [256][4]; else NULL */
 } moe_weights;
 
+/* Activations entering the routed experts' projections.
+ *  MOE_ACT_BF16   the bf16 tokens and an fp32 SwiGLU output, as given.
+ *  MOE_ACT_MXFP8  the A8 variant for MXFP4 experts: both are first quantized
+ *                 to OCP MX-FP8 -- per 32 consecutive values along K an E8M0
+ *                 scale X = 2^(floor(log2 amax) - 8) and E4M3 elements, the
+ *                 nearest to v / X (ties to an even mantissa, saturating at
+ *                 448; amax == 0 gives scale byte 0 and zero elements) -- and
+ *                 multiplied with the raw FP4 weights on the FP4 matrix
+ *                 instructions.  MXFP4 gate/up/down only; H, I multiples of
+ *                 512.  (hysenlabs.com ds4 page, "Model support and
+ *                 quantization": the MXFP4 variant keeps the released FP4
+ *                 experts.) */
+enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP8 = 1 };
+
 /* One MoE FFN layer.  gate/up are [E][I][H], down is [E][H][I]; the shared
  * expert (optional: NULL pointers or I_shared == 0) is bf16 [I_shared][H],
- * [I_shared][H], [H][I_shared]; the router is bf16 [E][H]. */
+ * [I_shared][H], [H][I_shared]; the router is bf16 [E][H].  act_fmt: a
+ * MOE_ACT_* value for the routed experts (the shared expert is always bf16). */
 typedef struct {
   int32_t H, I, E, k, I_shared, route_mode;
   const uint16_t *w_router;
   moe_weights gate, up, down;
   const uint16_t *shared_gate, *shared_up, *shared_down;
+  int32_t act_fmt;
 } moe_layer;
 
 /* Text of the last error on the calling thread ("" if none). */
@@ -140,15 +156,18 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
  *   moe_dispatch; expert_offsets == NULL means one dense expert (expert 0
  *   of the weights) applied to all T tokens in order (n_rows == T,
  *   sorted_token ignored) -- the shared expert.
+ * act_fmt: MOE_ACT_BF16, or MOE_ACT_MXFP8 (see above; MOE_EUNSUPPORTED
+ *   unless every projection is MXFP4 and H, I are multiples of 512).
  * y_rows: fp32 [n_rows][H] out.
  * Accumulation is fp32.  Small buckets (decode) run dequant-fused GEMVs;
- * large ones a grouped GEMM on matrix cores. */
+ * large ones a grouped GEMM on matrix cores; MOE_ACT_MXFP8 always the
+ * FP4 matrix instructions. */
 size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
-                                int fmt_down);
+                                int fmt_down, int act_fmt);
 int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
-                   const moe_weights *up, const moe_weights *down, const int32_t *expert_offsets,
-                   const int32_t *sorted_token, int n_rows, float *y_rows, void *ws,
-                   size_t ws_bytes, void *stream);
+                   const moe_weights *up, const moe_weights *down, int act_fmt,
+                   const int32_t *expert_offsets, const int32_t *sorted_token, int n_rows,
+                   float *y_rows, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_combine: the gather form of the weighted scatter-add:
@@ -190,6 +209,12 @@ int moe_forward_marked(const moe_layer *layer, int T, const uint16_t *x, const f
                        moe_mark *marks, int max_marks, int *n_marks, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* moe_mxfp8_quantize: the MOE_ACT_MXFP8 quantization of bf16 rows, as the
+ * A8 path applies it to the tokens.  x: bf16 [rows][K]; q: E4M3 codes
+ * uint8 [rows][K] out; scales: E8M0 uint8 [rows][K/32] out.  K % 32 == 0. */
+int moe_mxfp8_quantize(int rows, int K, const uint16_t *x, uint8_t *q, uint8_t *scales,
+                       void *stream);
+
 /* moe_dequantize: weights [w0, w0+count) of expert `expert`'s row-major
  * flattened matrix, decoded to fp32 with the same device decoders the FFN
  * kernels use.  out: fp32 [count]. */

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 FMT_BF16, FMT_Q2K, FMT_VQ2, FMT_MXFP4 = 0, 1, 2, 3
 ROUTE_SOFTMAX_TOPK, ROUTE_HASH = 0, 1
+ACT_BF16, ACT_MXFP8 = 0, 1
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 
 
@@ -37,7 +38,7 @@ class Layer(C.Structure):
                 ("I_shared", C.c_int32), ("route_mode", C.c_int32), ("w_router", C.c_void_p),
                 ("gate", Weights), ("up", Weights), ("down", Weights),
                 ("shared_gate", C.c_void_p), ("shared_up", C.c_void_p),
-                ("shared_down", C.c_void_p)]
+                ("shared_down", C.c_void_p), ("act_fmt", C.c_int32)]
 
 
 class Mark(C.Structure):
@@ -71,9 +72,10 @@ def lib():
         L.moe_dispatch_workspace.argtypes = [i32, i32, i32]
         L.moe_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn_workspace.restype = sz
-        L.moe_expert_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.moe_expert_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.moe_expert_ffn.argtypes = [i32, i32, i32, vp, C.POINTER(Weights), C.POINTER(Weights),
-                                     C.POINTER(Weights), vp, vp, i32, vp, vp, sz, vp]
+                                     C.POINTER(Weights), i32, vp, vp, i32, vp, vp, sz, vp]
+        L.moe_mxfp8_quantize.argtypes = [i32, i32, vp, vp, vp, vp]
         L.moe_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.moe_forward_workspace.restype = sz
         L.moe_forward_workspace.argtypes = [C.POINTER(Layer), i32]
@@ -161,16 +163,17 @@ class DeviceLayer:
     """A whole MoE layer in device memory, with its moe_layer descriptor."""
 
     def __init__(self, H, I, E, k, route_mode, w_router, gate, up, down,
-                 shared_gate=None, shared_up=None, shared_down=None):
+                 shared_gate=None, shared_up=None, shared_down=None, act=ACT_BF16):
         self.H, self.I, self.E, self.k, self.route_mode = H, I, E, k, route_mode
+        self.act = act
         self.w_router, self.gate, self.up, self.down = w_router, gate, up, down
         self.shared_gate, self.shared_up, self.shared_down = shared_gate, shared_up, shared_down
         self.I_shared = 0 if shared_gate is None else shared_gate.shape[0]
         self.c = Layer(H, I, E, k, self.I_shared, route_mode, _ptr(w_router), gate.c, up.c, down.c,
-                       _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down))
+                       _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), act)
 
     @classmethod
-    def upload(cls, layer, route_mode=ROUTE_SOFTMAX_TOPK, device="cuda"):
+    def upload(cls, layer, route_mode=ROUTE_SOFTMAX_TOPK, device="cuda", act=ACT_BF16):
         """From a host layer (fields spec, w_router, gate, up, down, shared_*, codebook)."""
         s = layer.spec
 
@@ -184,18 +187,26 @@ class DeviceLayer:
                    DeviceProj.upload(layer.gate, device, cb if layer.gate.fmt == FMT_VQ2 else None),
                    DeviceProj.upload(layer.up, device, cb if layer.up.fmt == FMT_VQ2 else None),
                    DeviceProj.upload(layer.down, device, cb if layer.down.fmt == FMT_VQ2 else None),
-                   u16(layer.shared_gate), u16(layer.shared_up), u16(layer.shared_down))
+                   u16(layer.shared_gate), u16(layer.shared_up), u16(layer.shared_down), act)
 
     def clone(self):
         """An independent copy of every weight (distinct device memory)."""
         cl = lambda t: None if t is None else t.clone()
         return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, cl(self.w_router),
                            self.gate.clone(), self.up.clone(), self.down.clone(),
-                           cl(self.shared_gate), cl(self.shared_up), cl(self.shared_down))
+                           cl(self.shared_gate), cl(self.shared_up), cl(self.shared_down),
+                           self.act)
 
     def with_route_mode(self, mode):
         return DeviceLayer(self.H, self.I, self.E, self.k, mode, self.w_router, self.gate,
-                           self.up, self.down, self.shared_gate, self.shared_up, self.shared_down)
+                           self.up, self.down, self.shared_gate, self.shared_up, self.shared_down,
+                           self.act)
+
+    def with_act(self, act):
+        """The same weights with another activation format (MOE_ACT_*)."""
+        return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, self.w_router,
+                           self.gate, self.up, self.down, self.shared_gate, self.shared_up,
+                           self.shared_down, act)
 
     def forward_workspace(self, T):
         return lib().moe_forward_workspace(C.byref(self.c), T)
@@ -244,7 +255,8 @@ def dispatch(topk_idx, E):
     return off, st, ss, sp
 
 
-def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows=None):
+def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows=None,
+               act=ACT_BF16):
     """moe_expert_ffn -> y_rows fp32 [n_rows, H] (dense over x when offsets is None)."""
     _dev(x, BF16, "x")
     _dev(expert_offsets, torch.int32, "expert_offsets")
@@ -254,11 +266,22 @@ def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows
     if n_rows is None:
         n_rows = T if expert_offsets is None else sorted_token.numel()
     y = torch.empty((n_rows, H), dtype=torch.float32, device=x.device)
-    ws = _ws(lib().moe_expert_ffn_workspace(T, n_rows, gate.E, H, I, gate.fmt, down.fmt), x.device)
+    ws = _ws(lib().moe_expert_ffn_workspace(T, n_rows, gate.E, H, I, gate.fmt, down.fmt, act),
+             x.device)
     _check(lib().moe_expert_ffn(T, H, I, _ptr(x), C.byref(gate.c), C.byref(up.c), C.byref(down.c),
-                                _ptr(expert_offsets), _ptr(sorted_token), n_rows, _ptr(y),
+                                act, _ptr(expert_offsets), _ptr(sorted_token), n_rows, _ptr(y),
                                 _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def mxfp8_quantize(x):
+    """moe_mxfp8_quantize -> (E4M3 codes uint8 [rows, K], E8M0 scales uint8 [rows, K/32])."""
+    _dev(x, BF16, "x")
+    rows, K = x.shape
+    q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_mxfp8_quantize(rows, K, _ptr(x), _ptr(q), _ptr(sc), _stream()))
+    return q, sc
 
 
 def combine(y_rows, slot_pos, topk_w, shared_y=None, want_bf16=False):

@@ -143,18 +143,21 @@ WView bf16_view(const uint16_t *p, int N, int K) {
 const char *const kRoutedGemmNames[3] = {"tile_list", "gemm_gateup", "gemm_down"};
 const char *const kSharedGemmNames[3] = {"shared_tile_list", "shared_gemm_gateup",
                                          "shared_gemm_down"};
+const char *const kA8Names[4] = {"tile_list", "a8_gemm_gateup", "a8_gemm_down", "act_quant"};
 
 struct FfnBufs {
   int32_t *plan;
   float *a;        // fp32 SwiGLU output of the GEMV path; fp16 on the GEMM path
   int32_t *tiles;  // GEMM tile list
+  void *a8;        // MX-FP8 tokens and SwiGLU output (MOE_ACT_MXFP8)
 };
 
-FfnBufs carve_ffn(Carver &c, int n_rows, int E, int I, bool dense) {
-  FfnBufs b;
+FfnBufs carve_ffn(Carver &c, int T, int n_rows, int E, int H, int I, bool dense, int act) {
+  FfnBufs b{};
   b.plan = dense ? nullptr : c.take<int32_t>(plan_ints(std::min(E, std::max(n_rows, 1))));
   b.a = c.take<float>((size_t)std::max(n_rows, 1) * I);
   b.tiles = c.take<int32_t>(gemm_tile_ints(std::max(n_rows, 1), dense ? 0 : E));
+  if (act == MOE_ACT_MXFP8) b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, std::max(n_rows, 1)));
   return b;
 }
 
@@ -174,10 +177,14 @@ bool use_gemm(int T, int H, int I, int E, int n_rows, bool dense, int fmt_gate, 
 }
 
 int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView &u,
-            const WView &d, const int32_t *offsets, const int32_t *sorted_token, int n_rows,
-            float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
+            const WView &d, int act, const int32_t *offsets, const int32_t *sorted_token,
+            int n_rows, float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
   Marker none;
   Marker &m = mk ? *mk : none;
+  if (act == MOE_ACT_MXFP8)
+    return hip_check(launch_a8_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
+                                   b.a8, y, s, mark_cb, &m, kA8Names),
+                     "a8 ffn");
   if (!offsets && skinny_supported(H, I, T, g, d))
     return hip_check(launch_skinny_ffn(g, u, d, H, I, T, x, reinterpret_cast<uint16_t *>(b.a), y,
                                        s, mark_cb, &m, kRoutedGemmNames),
@@ -217,6 +224,7 @@ struct FwdBufs {
   int32_t *tiles_sh;
   // small path
   int32_t *plan, *sorted_token, *slot_pos, *tiles;
+  void *a8;
   float *row_w, *a, *y_rows;
   // large path
   int32_t *offsets, *sorted_slot;
@@ -229,7 +237,7 @@ bool fwd_small(const moe_layer *L, int T) { return (long long)T * L->k <= kSmall
 bool has_shared(const moe_layer *L) { return L->I_shared > 0 && L->shared_gate; }
 
 bool fwd_decode1(const moe_layer *L, int T) {
-  return T == 1 && decode1_supported(L->H, L->I, has_shared(L) ? L->I_shared : 0, L->k);
+  return T == 1 && L->act_fmt == MOE_ACT_BF16 && decode1_supported(L->H, L->I, has_shared(L) ? L->I_shared : 0, L->k);
 }
 
 FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool have_idx,
@@ -258,6 +266,7 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.y_rows = c.take<float>(n * H);
     b.offsets = c.take<int32_t>(E + 1);
     b.tiles = c.take<int32_t>(gemm_tile_ints((int)n, E));
+    if (L->act_fmt == MOE_ACT_MXFP8) b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, (int)n));
   } else {
     b.offsets = c.take<int32_t>(E + 1);
     b.sorted_token = c.take<int32_t>(n);
@@ -265,9 +274,18 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.slot_pos = c.take<int32_t>(n);
     b.dispatch_ws = c.take<uint8_t>(dispatch_ws_bytes(T, E, k));
     b.y_rows = c.take<float>(n * H);
-    b.ffn = carve_ffn(c, (int)n, E, I, false);
+    b.ffn = carve_ffn(c, T, (int)n, E, H, I, false, L->act_fmt);
   }
   return b;
+}
+
+int check_act(int act, int H, int I, const moe_weights *g, const moe_weights *u,
+              const moe_weights *d) {
+  if (act == MOE_ACT_BF16) return MOE_OK;
+  if (act != MOE_ACT_MXFP8) return fail(MOE_EINVAL, "unknown act_fmt %d", act);
+  if (!a8_supported(H, I, view_of(*g), view_of(*u), view_of(*d)))
+    return fail(MOE_EUNSUPPORTED, "MX-FP8 activations need MXFP4 weights and H, I %% 512 == 0");
+  return MOE_OK;
 }
 
 int check_layer(const moe_layer *L) {
@@ -277,6 +295,7 @@ int check_layer(const moe_layer *L) {
   if (!L->w_router) return fail(MOE_EINVAL, "null router");
   if (!aligned(L->w_router, 16) || L->H % 8) return fail(MOE_EINVAL, "router misaligned");
   MOE_TRY(check_ffn_weights(L->E, L->H, L->I, &L->gate, &L->up, &L->down));
+  MOE_TRY(check_act(L->act_fmt, L->H, L->I, &L->gate, &L->up, &L->down));
   if (L->I_shared < 0) return fail(MOE_EINVAL, "I_shared < 0");
   if (L->I_shared > 0 && L->shared_gate) {
     if (!L->shared_up || !L->shared_down) return fail(MOE_EINVAL, "incomplete shared expert");
@@ -365,35 +384,37 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
 }
 
 size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
-                                int fmt_down) {
-  (void)T, (void)H, (void)fmt_gate, (void)fmt_down;
-  if (n_rows < 0 || E < 1 || I < 1) return 0;
+                                int fmt_down, int act_fmt) {
+  (void)fmt_gate, (void)fmt_down;
+  if (T < 0 || n_rows < 0 || E < 1 || I < 1 || H < 1) return 0;
   Carver c(nullptr);
-  carve_ffn(c, n_rows, E, I, false);
+  carve_ffn(c, T, n_rows, E, H, I, false, act_fmt);
   return c.size();
 }
 
 int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
-                   const moe_weights *up, const moe_weights *down, const int32_t *expert_offsets,
-                   const int32_t *sorted_token, int n_rows, float *y_rows, void *ws,
-                   size_t ws_bytes, void *stream) {
+                   const moe_weights *up, const moe_weights *down, int act_fmt,
+                   const int32_t *expert_offsets, const int32_t *sorted_token, int n_rows,
+                   float *y_rows, void *ws, size_t ws_bytes, void *stream) {
   if (T < 0 || n_rows < 0) return fail(MOE_EINVAL, "negative T or n_rows");
   if (!gate) return fail(MOE_EINVAL, "null gate");
   const int E = gate->n_experts;
   MOE_TRY(check_ffn_weights(E, H, I, gate, up, down));
+  MOE_TRY(check_act(act_fmt, H, I, gate, up, down));
   if (T == 0 || n_rows == 0) return MOE_OK;
   if (!x || !y_rows) return fail(MOE_EINVAL, "null x or y_rows");
   if (!aligned(x, 16) || !aligned(y_rows, 16)) return fail(MOE_EINVAL, "x/y_rows misaligned");
   const bool dense = expert_offsets == nullptr;
   if (dense && n_rows != T) return fail(MOE_EINVAL, "dense call needs n_rows == T");
   if (!dense && !sorted_token) return fail(MOE_EINVAL, "null sorted_token");
-  const size_t need = moe_expert_ffn_workspace(T, n_rows, E, H, I, gate->fmt, down->fmt);
+  const size_t need =
+      moe_expert_ffn_workspace(T, n_rows, E, H, I, gate->fmt, down->fmt, act_fmt);
   if (!ws || ws_bytes < need)
     return fail(MOE_ENOSPC, "expert_ffn workspace: %zu bytes < %zu", ws_bytes, need);
   Carver c(ws);
-  FfnBufs b = carve_ffn(c, n_rows, E, I, dense);
-  return run_ffn(T, H, I, x, view_of(*gate), view_of(*up), view_of(*down), expert_offsets,
-                 sorted_token, n_rows, y_rows, b, as_stream(stream));
+  FfnBufs b = carve_ffn(c, T, n_rows, E, H, I, dense, act_fmt);
+  return run_ffn(T, H, I, x, view_of(*gate), view_of(*up), view_of(*down), act_fmt,
+                 expert_offsets, sorted_token, n_rows, y_rows, b, as_stream(stream));
 }
 
 int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
@@ -497,7 +518,11 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, b.offsets,
                                     b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
                       "select"));
-    if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt)) {
+    if (L->act_fmt == MOE_ACT_MXFP8) {
+      MOE_TRY(hip_check(launch_a8_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n, b.tiles,
+                                      b.a8, b.y_rows, s, mark_cb, &mk, kA8Names),
+                        "a8 ffn"));
+    } else if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt)) {
       // several tokens: every selected expert's weights once, all its rows per load
       MOE_TRY(hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n,
                                         b.tiles, reinterpret_cast<uint16_t *>(b.a), b.y_rows, s,
@@ -524,7 +549,8 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
   MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
                                     b.slot_pos, b.dispatch_ws, s, mark_cb, &mk),
                     "dispatch"));
-  MOE_TRY(run_ffn(T, H, I, x, g, u, d, b.offsets, b.sorted_token, n, b.y_rows, b.ffn, s, &mk));
+  MOE_TRY(run_ffn(T, H, I, x, g, u, d, L->act_fmt, b.offsets, b.sorted_token, n, b.y_rows, b.ffn,
+                  s, &mk));
   mk("combine");
   return hip_check(
       launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
@@ -556,6 +582,15 @@ int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float
   return rc;
 }
 
+
+int moe_mxfp8_quantize(int rows, int K, const uint16_t *x, uint8_t *q, uint8_t *scales,
+                       void *stream) {
+  if (rows < 0 || K < 32 || K % 32) return fail(MOE_EINVAL, "bad rows = %d / K = %d", rows, K);
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return fail(MOE_EINVAL, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 8)) return fail(MOE_EINVAL, "x/q misaligned");
+  return hip_check(launch_mx8_quant(rows, K, x, q, scales, as_stream(stream)), "mxfp8 quantize");
+}
 
 int moe_dequantize(const moe_weights *w, int expert, int64_t w0, int64_t count, float *out,
                    void *stream) {

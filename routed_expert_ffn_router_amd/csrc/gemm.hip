@@ -601,6 +601,12 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_skinny(SkinnyArgs p) {
 
 // K a multiple of 256 (whole Q2K / VQ2 groups; a whole number of register
 // stages), output columns a multiple of the block's (128 a columns, 256 down)
+hipError_t launch_tile_list(int E, int n_dense, int bm, const int32_t *offsets, int32_t *tiles,
+                            hipStream_t s) {
+  launch(k_tile_list, dim3(1), dim3(1024), s, offsets ? E : 0, n_dense, bm, offsets, tiles);
+  return hipGetLastError();
+}
+
 bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
   (void)fmt_gate, (void)fmt_down;
   return H >= 256 && I >= 256 && H % 256 == 0 && I % 256 == 0;

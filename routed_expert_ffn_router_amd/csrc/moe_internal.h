@@ -120,6 +120,24 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
                            void (*mark)(void *, const char *), void *mark_ctx,
                            const char *const names[3]);
 
+// tile list of the grouped GEMMs: tiles of bm rows over the buckets
+// (offsets [E+1]), or over rows [0, n_dense) of one dense expert (offsets null)
+hipError_t launch_tile_list(int E, int n_dense, int bm, const int32_t *offsets, int32_t *tiles,
+                            hipStream_t s);
+
+// MXFP4 experts with MX-FP8 activations on the FP4 matrix instructions
+// (gemm_fp4.hip): ws of a8_ws_bytes(T, H, I, n_rows) holds the quantized
+// tokens and SwiGLU output; names: tile list, gate/up, down, quantization
+bool a8_supported(int H, int I, const WView &gate, const WView &up, const WView &down);
+size_t a8_ws_bytes(int T, int H, int I, int n_rows);
+hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
+                         int T, const uint16_t *x, const int32_t *offsets,
+                         const int32_t *sorted_token, int n_rows, int32_t *tiles, void *ws,
+                         float *y, hipStream_t s, void (*mark)(void *, const char *),
+                         void *mark_ctx, const char *const names[4]);
+hipError_t launch_mx8_quant(int rows, int K, const uint16_t *x, uint8_t *q, uint8_t *sc,
+                            hipStream_t s);
+
 // dense one-expert FFN of T <= 64 rows with bf16 weights (a small batch's
 // shared expert): a16 fp16 [T][I], y fp32 [T][H]
 bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down);

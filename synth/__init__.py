@@ -72,6 +72,7 @@ class Workload:
     T: int
     route: int = ROUTE_SOFTMAX_TOPK
     logits: str = "router"  # "router": computed from x and the router; "zipf": drawn
+    act: int = 0  # activations of the routed experts: 0 bf16, 1 MX-FP8 (the A8 variant)
 
 
 WORKLOADS = {
@@ -85,6 +86,8 @@ WORKLOADS = {
         Workload("mxfp4_hash_decode_b1", MX, 1, route=ROUTE_HASH),
         Workload("mxfp4_prefill_4096", MX, 4096),
         Workload("mxfp4_hash_prefill_4096", MX, 4096, route=ROUTE_HASH),
+        Workload("mxfp4_a8_prefill_4096", MX, 4096, act=1),
+        Workload("mxfp4_hash_a8_prefill_4096", MX, 4096, route=ROUTE_HASH, act=1),
     ]
 }
 

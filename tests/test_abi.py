@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
               "moe_dequantize", "moe_last_error", "moe_abi_version", "moe_route_workspace",
-              "moe_dispatch_workspace", "moe_expert_ffn_workspace", "moe_forward_workspace"]:
+              "moe_dispatch_workspace", "moe_expert_ffn_workspace", "moe_forward_workspace",
+              "moe_mxfp8_quantize"]:
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
 
 
 def _w(fmt=moe.FMT_VQ2, E=8, N=2048, K=4096, data=FAKE, scales=FAKE, cb=FAKE):
@@ -94,11 +95,11 @@ def test_expert_ffn_rejects_bad_arguments():
     lib = _lib()
     g, u, d = _w(), _w(), _w(moe.FMT_Q2K, 8, 4096, 2048, FAKE, None, None)
     f = lib.moe_expert_ffn
-    ws = lib.moe_expert_ffn_workspace(1, 8, 8, 4096, 2048, moe.FMT_VQ2, moe.FMT_Q2K)
+    ws = lib.moe_expert_ffn_workspace(1, 8, 8, 4096, 2048, moe.FMT_VQ2, moe.FMT_Q2K, 0)
 
-    def call(g=g, u=u, d=d, H=4096, I=2048, off=FAKE, st=FAKE, n=8, ws_=ws):
-        return f(1, H, I, FAKE, C.byref(g), C.byref(u), C.byref(d), off, st, n, FAKE, FAKE, ws_,
-                 None)
+    def call(g=g, u=u, d=d, H=4096, I=2048, off=FAKE, st=FAKE, n=8, ws_=ws, act=0):
+        return f(1, H, I, FAKE, C.byref(g), C.byref(u), C.byref(d), act, off, st, n, FAKE, FAKE,
+                 ws_, None)
 
     assert call(H=2048) == moe.EINVAL and "shape" in _err()
     assert call(u=_w(moe.FMT_MXFP4)) == moe.EUNSUPPORTED
@@ -114,6 +115,21 @@ def test_expert_ffn_rejects_bad_arguments():
     assert call(ws_=ws - 1) == moe.ENOSPC
     assert call(off=None, n=5) == moe.EINVAL and "n_rows == T" in _err()
     assert call(n=0) == moe.OK
+    # MX-FP8 activations: MXFP4 weights only, H and I multiples of 512
+    assert call(act=moe.ACT_MXFP8) == moe.EUNSUPPORTED and "MX-FP8" in _err()
+    assert call(act=7) == moe.EINVAL
+    mg = _w(moe.FMT_MXFP4, 8, 2048, 4096, FAKE, FAKE, None)
+    md = _w(moe.FMT_MXFP4, 8, 4096, 2048, FAKE, FAKE, None)
+    ws8 = lib.moe_expert_ffn_workspace(1, 8, 8, 4096, 2048, moe.FMT_MXFP4, moe.FMT_MXFP4,
+                                       moe.ACT_MXFP8)
+    assert ws8 > lib.moe_expert_ffn_workspace(1, 8, 8, 4096, 2048, moe.FMT_MXFP4,
+                                              moe.FMT_MXFP4, 0)
+    assert call(g=mg, u=mg, d=md, act=moe.ACT_MXFP8, ws_=ws8 - 1) == moe.ENOSPC
+    assert call(g=mg, u=mg, d=md, act=moe.ACT_MXFP8, n=0) == moe.OK
+    q = lib.moe_mxfp8_quantize
+    assert q(4, 100, FAKE, FAKE, FAKE, None) == moe.EINVAL
+    assert q(4, 128, None, FAKE, FAKE, None) == moe.EINVAL
+    assert q(0, 128, None, None, None, None) == moe.OK
 
 
 def test_combine_and_dequantize_reject_bad_arguments():

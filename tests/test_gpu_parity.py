@@ -234,19 +234,22 @@ def test_expert_ffn_dense_shared(dev, q2, dq2, T):
 # the whole layer
 # --------------------------------------------------------------------------
 
-def _forward_case(layer, dl, dev, T, seed, route=moe.ROUTE_SOFTMAX_TOPK, zipf=False):
+def _forward_case(layer, dl, dev, T, seed, route=moe.ROUTE_SOFTMAX_TOPK, zipf=False, a8=False):
     x = synth.gen_x(layer.spec.H, T, seed=seed)
     lg = synth.gen_zipf_logits(layer.spec.E, T, 1.1, seed=seed) if zipf else None
     tids = synth.gen_token_ids(T, seed=seed) if route == moe.ROUTE_HASH else None
-    ref, ref_idx, ref_w = oracle.LayerRef(layer, route_mode=route).forward(x, lg, tids)
+    ref, ref_idx, ref_w = oracle.LayerRef(layer, route_mode=route).forward(x, lg, tids, a8=a8)
     L = dl.with_route_mode(route)
     out, idx, w = moe.forward(L, t16(x, dev), None if lg is None else torch.from_numpy(lg).to(dev),
                               None if tids is None else torch.from_numpy(tids).to(dev))
     out, idx, w = tnp(out), tnp(idx), tnp(w)
     assert np.array_equal(idx, ref_idx)
     np.testing.assert_allclose(w, ref_w, rtol=1e-6, atol=1e-7)
-    err = normwise(out, ref)
-    assert err < TOL, err
+    if a8:
+        _assert_a8_close(layer, x, ref_idx, ref_w, out, ref)
+    else:
+        err = normwise(out, ref)
+        assert err < TOL, err
     return out
 
 
@@ -381,7 +384,7 @@ def test_expert_ffn_dense_shared_gemm(dev, q2, dq2, T):
 
 
 def _forward_sampled(layer, dl, dev, T, seed, n_sample, route=moe.ROUTE_SOFTMAX_TOPK,
-                     zipf=False):
+                     zipf=False, a8=False):
     """Full-size forward on the GPU; routing of every token bit-exact against the
     oracle, outputs of sampled tokens within the tolerance."""
     x = synth.gen_x(layer.spec.H, T, seed=seed)
@@ -399,9 +402,12 @@ def _forward_sampled(layer, dl, dev, T, seed, n_sample, route=moe.ROUTE_SOFTMAX_
     rng = np.random.default_rng(seed + 1)
     sel = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
     ref, _, _ = R.forward(x[sel], None if lg is None else lg[sel],
-                          None if tids is None else tids[sel])
-    err = normwise(out[sel], ref)
-    assert err < TOL, err
+                          None if tids is None else tids[sel], a8=a8)
+    if a8:
+        _assert_a8_close(layer, x[sel], idx[sel], w[sel], out[sel], ref)
+    else:
+        err = normwise(out[sel], ref)
+        assert err < TOL, err
 
 
 def test_forward_prefill_2048(dev, q2, dq2):
@@ -415,3 +421,164 @@ def test_forward_q2_zipf_gemm(dev, q2, dq2):
 @pytest.mark.parametrize("route", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
 def test_forward_mxfp4_prefill_4096(dev, mx, dmx, route):
     _forward_sampled(mx, dmx, dev, 4096, 4096 + route, 6, route=route)
+
+
+# --------------------------------------------------------------------------
+# MX-FP8 activations on the FP4 matrix instructions (the A8 variant)
+#
+# The tokens' quantization is compared bit-exact (same inputs on both sides).
+# The SwiGLU output is quantized from values the GPU accumulates in fp32 and
+# the oracle in fp64 (where every product and sum is exact), so an element
+# lying within fp32 error of an E4M3 rounding midpoint may take either
+# neighbouring code on the GPU -- both are correct A8 results.  The layer
+# output is therefore compared elementwise within TOL * max|ref| plus the
+# most those ambiguous decisions can move it: for each ambiguous element,
+# one E4M3 step times |W_down| times the routing weight (a group whose
+# largest magnitude is that close to a power of two may also take the
+# neighbouring scale).  Everything else must agree to TOL.
+# --------------------------------------------------------------------------
+
+_E4M3 = None
+
+
+def _e4m3_values():
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = np.array([oracle.e4m3(c) for c in range(256)], np.float64)
+    return _E4M3
+
+
+def _chunked_error(X, W, chunk=32):
+    """Rounding-error bound of a product X W^T accumulated in fp32 with a
+    rounding at most every 32 products (one E8M0 scale block; each FP4
+    matrix instruction sums 4 of them): every chunk's sum rounded once and
+    added to the running fp32 sum with one more rounding:
+    2^-24 (sum_c |chunk sum_c| + sum_c |running sum_c|)."""
+    K = X.shape[1]
+    run = np.zeros((X.shape[0], W.shape[0]))
+    bound = np.zeros_like(run)
+    for c in range(0, K, chunk):
+        part = X[:, c:c + chunk] @ W[:, c:c + chunk].T
+        run += part
+        bound += np.abs(part) + np.abs(run)
+    return 2.0 ** -24 * bound
+
+
+def _a8_ambiguity(layer, x, idx, w):
+    """[T][H] bound on the output change from ambiguous MX-FP8 decisions on
+    the SwiGLU output (see above).  The GPU's gate/up sums may differ from
+    the exact ones by twice the accumulation bound of _chunked_error; the
+    SwiGLU in fp32 adds 2^-20 relative."""
+    spec = layer.spec
+    H, I = spec.H, spec.I
+    xv = (x.astype(np.uint32) << 16).view(np.float32)
+    codes, sc = oracle.mxfp8_quant(xv)
+    xq = _e4m3_values()[codes] * np.exp2(np.repeat(sc.astype(np.float64) - 127.0, 32, axis=1))
+    T = x.shape[0]
+    B = np.zeros((T, H))
+    pairs = {}
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            pairs.setdefault(int(idx[t, j]), []).append((t, j))
+    n_amb = 0
+    for e, tj in pairs.items():
+        G = oracle.dequant_matrix(layer.gate, e).astype(np.float64)
+        U = oracle.dequant_matrix(layer.up, e).astype(np.float64)
+        D = np.abs(oracle.dequant_matrix(layer.down, e).astype(np.float64))
+        X = xq[[t for t, _ in tj]]
+        g, u = X @ G.T, X @ U.T
+        eg, eu = 2 * _chunked_error(X, G), 2 * _chunked_error(X, U)
+        sig = 1.0 / (1.0 + np.exp(-g))
+        silu = g * sig
+        a = silu * u
+        da = (np.abs(sig * (1 + g * (1 - sig))) * eg * np.abs(u) + np.abs(silu) * eu
+              + 2.0 ** -20 * np.abs(a))
+        n = len(tj)
+        ag, dg = np.abs(a).reshape(n, I // 32, 32), da.reshape(n, I // 32, 32)
+        amax = ag.max(axis=2)
+        safe = np.where(amax > 0, amax, 1.0)
+        Xs = np.exp2(np.clip(np.floor(np.log2(safe)) - 8, -127, 127))[:, :, None]
+        y = ag / Xs
+        step = np.exp2(np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3)
+        dist = np.abs(y / step - np.floor(y / step) - 0.5) * step * Xs
+        delta = np.where((dist <= dg) & (y < 448), step * Xs, 0.0)
+        p2 = np.exp2(np.round(np.log2(safe)))
+        damax = np.take_along_axis(dg, ag.argmax(axis=2)[:, :, None], 2)[:, :, 0]
+        samb = (amax > 0) & (np.abs(amax - p2) <= damax)
+        delta = np.where(samb[:, :, None], 0.25 * ag + 2 * step * Xs, delta)
+        n_amb += int((delta > 0).sum())
+        contrib = delta.reshape(n, I) @ D.T
+        for r, (t, j) in enumerate(tj):
+            B[t] += float(w[t, j]) * contrib[r]
+    return B, n_amb
+
+
+def _assert_a8_close(layer, x, idx, w, out, ref):
+    B, n_amb = _a8_ambiguity(layer, x, idx, w)
+    base = TOL * np.abs(ref).max()
+    excess = np.abs(out.astype(np.float64) - ref) - (base + B)
+    assert (excess <= 0).all(), (float(excess.max()), normwise(out, ref), n_amb)
+    # the ambiguous decisions are a small minority of the SwiGLU elements
+    assert n_amb <= 0.01 * x.shape[0] * idx.shape[1] * layer.spec.I, n_amb
+
+def _bf16_round(v):
+    """fp32 -> bf16 bit patterns, round to nearest even (no NaNs here)."""
+    u = np.ascontiguousarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_mxfp8_quantize_bit_exact(dev):
+    """Codes and scales of the device quantizer equal the oracle's, on wide
+    magnitude ranges and hand-made groups: all zeros, saturation (scaled
+    values in [448, 512)), ties between E4M3 neighbours (normal and
+    subnormal), signed values, bf16 subnormals."""
+    rng = np.random.default_rng(7)
+    rows, K = 96, 1024
+    v = (rng.standard_normal((rows, K)) * np.exp2(rng.integers(-30, 30, (rows, 1)))).astype(np.float32)
+    v[0, :32] = 0.0
+    v[1, :32] = 496.0 * (1 - 2 * (np.arange(32) % 2))       # amax 496: X = 1, all saturate
+    v[2, :32] = 1.0                                          # X = 2^-8
+    g = np.zeros(32, np.float32)                             # X = 1 (amax 256): exact ties
+    g[:8] = [256.0, 1.0625, 1.1875, -1.0625, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 2.0 ** -9, 15.5]
+    v[3, :32] = g
+    v[4, :32] = np.float32(2.0 ** -130) * (1 + np.arange(32) % 3)   # bf16 subnormals
+    v[5, :] = -np.abs(v[5, :])
+    bits = _bf16_round(v)
+    q, sc = moe.mxfp8_quantize(t16(bits, dev))
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    rq, rs = oracle.mxfp8_quant(vals)
+    assert np.array_equal(tnp(sc), rs)
+    assert np.array_equal(tnp(q), rq)
+
+
+@pytest.mark.parametrize("T", [1, 3, 40, 300])
+def test_forward_mxfp4_a8(dev, mx, dmx, T):
+    _forward_case(mx, dmx.with_act(moe.ACT_MXFP8), dev, T, 500 + T, a8=True)
+
+
+def test_forward_mxfp4_a8_hash(dev, mx, dmx):
+    _forward_case(mx, dmx.with_act(moe.ACT_MXFP8), dev, 100, 601, route=moe.ROUTE_HASH, a8=True)
+
+
+@pytest.mark.parametrize("route", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
+def test_forward_mxfp4_a8_prefill_4096(dev, mx, dmx, route):
+    _forward_sampled(mx, dmx.with_act(moe.ACT_MXFP8), dev, 4096, 7000 + route, 6, route=route,
+                     a8=True)
+
+
+def test_forward_a8_equals_composed_calls(dev, mx, dmx):
+    """moe_forward with MX-FP8 activations vs the four calls with act_fmt set."""
+    T = 70
+    L = dmx.with_act(moe.ACT_MXFP8)
+    x = t16(synth.gen_x(4096, T, seed=9), dev)
+    out, idx, w = moe.forward(L, x)
+    idx2, w2, _ = moe.route(x, L.w_router, 8)
+    off, st, ss, sp = moe.dispatch(idx2, 256)
+    y = moe.expert_ffn(x, L.gate, L.up, L.down, off, st, act=moe.ACT_MXFP8)
+    sg = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, L.shared_gate)
+    su = moe.DeviceProj(moe.FMT_BF16, 1, 2048, 4096, L.shared_up)
+    sd = moe.DeviceProj(moe.FMT_BF16, 1, 4096, 2048, L.shared_down)
+    sh = moe.expert_ffn(x, sg, su, sd)
+    out2, _ = moe.combine(y, sp, w2, sh)
+    assert np.array_equal(tnp(idx), tnp(idx2))
+    assert normwise(tnp(out2), tnp(out).astype(np.float64)) < 1e-5
