@@ -198,12 +198,14 @@ def kernel_cost(name, L, T, U, n):
     xb = T * H * 2
     table = {
         # fused batch-1 decode: (1) shared gate/up + router, (2) shared down +
-        # select + routed gate/up, (3) routed down + combine
+        # select + routed gate/up, (3) routed down + combine with the shared row
         "decode_p1": (2 * Is * H * 2 + E * H * 2 + xb + Is * 4 + E * 4,
                       2 * T * (2 * Is * H + E * H)),
-        "decode_p2": (U * gu + cb + xb + E * 4 + n * I * 4 + n * 8, 4 * n * I * H),
-        "decode_p3": (U * dn + H * Is * 2 + Is * 4 + n * I * 4 + n * 8 + T * H * 4,
-                      2 * n * H * I + 2 * T * H * Is),
+        "decode_p2": (U * gu + cb + xb + E * 4 + n * I * 4 + n * 8
+                      + H * Is * 2 + Is * 4 + T * H * 4,
+                      4 * n * I * H + 2 * T * H * Is),
+        "decode_p3": (U * dn + T * H * 4 + n * I * 4 + n * 8 + T * H * 4,
+                      2 * n * H * I),
         "router": (E * H * 2 + xb + T * E * 4, 2 * T * E * H),
         "shared_gateup": (2 * Is * H * 2 + xb + T * Is * 4, 4 * T * Is * H),
         "shared_down": (H * Is * 2 + T * Is * 4 + T * H * 4, 2 * T * H * Is),

@@ -472,7 +472,7 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
       a.su = bf16_view(L->shared_up, a.Is, H);
       a.sd = bf16_view(L->shared_down, H, a.Is);
     }
-    a.logits = b.logits, a.a_sh = b.a_sh, a.a = b.a;
+    a.logits = b.logits, a.a_sh = b.a_sh, a.a = b.a, a.shared_y = b.shared_y;
     // the split forms reuse the fp32 buffers: two uint16 halves per float
     a.a_sh_hi = reinterpret_cast<uint16_t *>(b.a_sh);
     a.a_sh_lo = a.Is ? a.a_sh_hi + a.Is : nullptr;

@@ -9,13 +9,12 @@
 //   p1: shared gate/up + SwiGLU (8 waves per block, a row pair each) and the
 //       router logits (a ninth wave per block, one expert row, fp64)
 //   p2: top-k selection, recomputed by every block from the logits (no
-//       separate launch), then routed gate/up + SwiGLU for its tile
-//   p3: routed down of the k experts (one expert per wave) + shared down
-//       (four more waves) + weighted sum, reduced in a fixed order
-//       (deterministic, no atomics)
-// Nothing with a dependency shares a launch with the bulk stream it would
-// queue behind: p2 holds only the routed weights, whose loads wait for the
-// selection anyway, and the shared down rides with the routed down in p3.
+//       separate launch), then routed gate/up + SwiGLU for its tile; every
+//       wave first requests one row of the shared down, which streams while
+//       the selection leaves the routed weights waiting
+//   p3: routed down of the k experts (one expert per wave) + weighted sum
+//       with the shared down, reduced in a fixed order (deterministic, no
+//       atomics)
 #include "select.h"
 
 namespace moe {
@@ -23,9 +22,11 @@ namespace moe {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kP1Threads = kDecThreads + 64;  // + the router wave
-constexpr int kP3Rows = 16;                   // output rows per p3 block
-constexpr int kP3SharedWaves = 4;             // shared-down waves per p3 block
-constexpr int kP3Threads = 64 * (kDecWaves + kP3SharedWaves);
+// output rows per p3 block: 16 (two rounds of eight rows in flight per wave)
+// for the small Q2K/VQ2 chunks, 8 for MXFP4 and bf16
+template <int DFMT>
+constexpr int p3_rows() { return DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_VQ2 ? 16 : 8; }
+constexpr int kP3Threads = kDecThreads;
 constexpr int kRouterChunks = 8;              // H <= 64 lanes x 8 bf16 x 8
 
 // ---------------------------------------------------------------------------
@@ -87,10 +88,11 @@ __global__ __launch_bounds__(kP1Threads) void k_dec_p1(DecodeArgs p) {
 
 // ---------------------------------------------------------------------------
 // p2: block b: routed gate/up tile b (expert slot b / tiles, 8 waves x ST
-// rows).  The selection's inputs are fetched and waited for before any weight
-// load goes out; wave 0 then selects while the others fill the codebook.
+// rows).  The selection's inputs are fetched first, then each wave's shared
+// down row; wave 0 selects while the others fill the codebook, and after the
+// block barrier each wave finishes its shared row before its routed rows.
 // ---------------------------------------------------------------------------
-template <int RFMT, int RSPL>
+template <int RFMT, int RSPL, int SSPL>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_p2(DecodeArgs p) {
   __shared__ uint2 s_cb[RFMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   __shared__ int s_e[16];
@@ -106,6 +108,15 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int64_t tid0 = *(p.tid ? p.tid : reinterpret_cast<const int64_t *>(p.x));
   uint32_t cbw = 0;
   if constexpr (RFMT == MOE_FMT_VQ2) cbw = codebook_entry_load(p.gate.codebook);
+  // then this wave's shared down row gw (the wave's own, independent of the
+  // selection: it streams while the selection runs) and p1's SwiGLU output
+  const int gw = blockIdx.x * kDecWaves + wave;
+  Chunk<MOE_FMT_BF16, SSPL, 64> csh;
+  ADown<MOE_FMT_BF16, SSPL, 64> ash[1];
+  if (p.Is) {
+    csh.load(p.sd, 0, min(gw, p.H - 1), lane);
+    ash[0].load_split(p.a_sh_hi, p.a_sh_lo, lane);
+  }
   asm volatile("" ::"v"(cbw), "v"(lg.v[0]), "v"(lg.v[1]), "v"(lg.v[2]), "v"(lg.v[3]),
                "v"((uint32_t)tid0), "v"((uint32_t)(tid0 >> 32)));
   if constexpr (RFMT == MOE_FMT_VQ2) codebook_entry_store<kDecThreads>(cbw, s_cb);
@@ -125,6 +136,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
   __syncthreads();
+  // the shared down rows gw, gw + 8 nb, ... (their data is in by now)
+  if (p.Is) {
+    for (int r = gw; r < p.H; r += gridDim.x * kDecWaves) {
+      if (r != gw) csh.load(p.sd, 0, r, lane);
+      float y[1];
+      csh.template dot_a<1>(ash, nullptr, y);
+      y[0] = wave_sum_f(y[0]);
+      if (lane == 0) p.shared_y[r] = y[0];
+    }
+  }
   constexpr int ST = steps_for<RFMT, RSPL>();
   const int j = blockIdx.x / p.tiles_per_expert, tile = blockIdx.x % p.tiles_per_expert;
   const int row_base = (tile * kDecWaves + wave) * ST;
@@ -137,16 +158,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
 }
 
 // ---------------------------------------------------------------------------
-// p3: block b owns output rows [16 b, 16 b + 16).  Waves 0..7: routed down of
-// expert j = wave (+ 8 ...) over those rows, weighted by w_j; waves 8..11: the
-// shared down of four rows each.  Thread r < 16 then adds the eight routed
-// partial sums in wave order and the shared value.
+// p3: block b owns output rows [R b, R b + R), R = p3_rows.  Wave w: routed
+// down of expert j = w (+ 8 ...) over those rows, weighted by w_j.  Thread
+// r < R
+// then adds the eight routed partial sums in wave order and p2's shared down.
 // ---------------------------------------------------------------------------
-template <int DFMT, int DSPL, int SSPL>
+template <int DFMT, int DSPL>
 __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
+  constexpr int kP3Rows = p3_rows<DFMT>();
   __shared__ uint2 s_cb[DFMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   __shared__ float s_part[kDecWaves][kP3Rows];
-  __shared__ float s_sh[kP3Rows];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = blockIdx.x * kP3Rows;
@@ -154,30 +175,11 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
     fill_codebook(p.down.codebook, s_cb);
     __syncthreads();
   }
-  if (wave >= kDecWaves) {  // shared down: rows row0 + 4 (wave - 8) + r
-    constexpr int R = kP3Rows / kP3SharedWaves;
-    const int rb = row0 + R * (wave - kDecWaves);
-    if (p.Is) {
-      Chunk<MOE_FMT_BF16, SSPL, 64> c[R];
-#pragma unroll
-      for (int r = 0; r < R; r++) c[r].load(p.sd, 0, min(rb + r, p.H - 1), lane);
-      ADown<MOE_FMT_BF16, SSPL, 64> av[1];
-      av[0].load_split(p.a_sh_hi, p.a_sh_lo, lane);
-#pragma unroll
-      for (int r = 0; r < R; r++) {
-        float y[1];
-        c[r].template dot_a<1>(av, nullptr, y);
-        y[0] = wave_sum_f(y[0]);
-        if (lane == 0) s_sh[rb - row0 + r] = y[0];
-      }
-    } else if (lane < R) {
-      s_sh[rb - row0 + lane] = 0.0f;
-    }
-  } else {
+  {
     // rows whose loads are in flight per wave: eight when their raw bits fit
-    // in about 48 registers (not MXFP4's wider chunks), else two
+    // in about 48 registers (not MXFP4's wider chunks), else four
     constexpr int kDw = DFMT == MOE_FMT_BF16 ? 8 * DSPL : DFMT == MOE_FMT_VQ2 ? 2 * DSPL : 3 * DSPL;
-    constexpr int PF = DFMT != MOE_FMT_MXFP4 && 48 / kDw >= 8 ? 8 : 2;
+    constexpr int PF = DFMT != MOE_FMT_MXFP4 && 48 / kDw >= 8 ? 8 : 4;
     const uint2 *cb = s_cb + (lane % kNCopy);
     float acc[kP3Rows];
 #pragma unroll
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < kDecWaves; w++) v += s_part[w][r];
-      v += s_sh[r];
+      if (p.Is) v += p.shared_y[row];
       p.out[row] = v;
       if (p.out_bf16) p.out_bf16[row] = (uint16_t)f32_to_bf16_bits(v);
     }
@@ -235,33 +237,25 @@ int spl_of(int K) {
   return spl;
 }
 
-template <int RFMT>
-hipError_t p2_fmt(const DecodeArgs &a, int rspl, hipStream_t s) {
-  if (rspl == 4)
-    launch(k_dec_p2<RFMT, 4>, dim3(a.nb_routed), dim3(kDecThreads), s, a);
-  else if (rspl == 2)
-    launch(k_dec_p2<RFMT, 2>, dim3(a.nb_routed), dim3(kDecThreads), s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+template <int RFMT, int RSPL>
+hipError_t p2_shared(const DecodeArgs &a, int sspl, hipStream_t s) {
+  if (sspl == 4) return launch(k_dec_p2<RFMT, RSPL, 4>, dim3(a.nb_routed), dim3(kDecThreads), s, a);
+  if (sspl == 2) return launch(k_dec_p2<RFMT, RSPL, 2>, dim3(a.nb_routed), dim3(kDecThreads), s, a);
+  return hipErrorInvalidValue;
 }
 
-template <int DFMT, int DSPL>
-hipError_t p3_shared(const DecodeArgs &a, int sspl, hipStream_t s) {
-  const dim3 grid((a.H + kP3Rows - 1) / kP3Rows);
-  if (sspl == 4)
-    launch(k_dec_p3<DFMT, DSPL, 4>, grid, dim3(kP3Threads), s, a);
-  else if (sspl == 2)
-    launch(k_dec_p3<DFMT, DSPL, 2>, grid, dim3(kP3Threads), s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+template <int RFMT>
+hipError_t p2_fmt(const DecodeArgs &a, int rspl, int sspl, hipStream_t s) {
+  if (rspl == 4) return p2_shared<RFMT, 4>(a, sspl, s);
+  if (rspl == 2) return p2_shared<RFMT, 2>(a, sspl, s);
+  return hipErrorInvalidValue;
 }
 
 template <int DFMT>
-hipError_t p3_fmt(const DecodeArgs &a, int dspl, int sspl, hipStream_t s) {
-  if (dspl == 2) return p3_shared<DFMT, 2>(a, sspl, s);
-  if (dspl == 4) return p3_shared<DFMT, 4>(a, sspl, s);
+hipError_t p3_fmt(const DecodeArgs &a, int dspl, hipStream_t s) {
+  const dim3 grid((a.H + p3_rows<DFMT>() - 1) / p3_rows<DFMT>());
+  if (dspl == 2) return launch(k_dec_p3<DFMT, 2>, grid, dim3(kP3Threads), s, a);
+  if (dspl == 4) return launch(k_dec_p3<DFMT, 4>, grid, dim3(kP3Threads), s, a);
   return hipErrorInvalidValue;
 }
 
@@ -308,18 +302,18 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
   }
   mark(mark_ctx, "decode_p2");
   switch (a.gate.fmt) {
-    case MOE_FMT_BF16: e = p2_fmt<MOE_FMT_BF16>(a, hs, s); break;
-    case MOE_FMT_Q2K: e = p2_fmt<MOE_FMT_Q2K>(a, hs, s); break;
-    case MOE_FMT_VQ2: e = p2_fmt<MOE_FMT_VQ2>(a, hs, s); break;
-    default: e = p2_fmt<MOE_FMT_MXFP4>(a, hs, s); break;
+    case MOE_FMT_BF16: e = p2_fmt<MOE_FMT_BF16>(a, hs, ss, s); break;
+    case MOE_FMT_Q2K: e = p2_fmt<MOE_FMT_Q2K>(a, hs, ss, s); break;
+    case MOE_FMT_VQ2: e = p2_fmt<MOE_FMT_VQ2>(a, hs, ss, s); break;
+    default: e = p2_fmt<MOE_FMT_MXFP4>(a, hs, ss, s); break;
   }
   if (e != hipSuccess) return e;
   mark(mark_ctx, "decode_p3");
   switch (a.down.fmt) {
-    case MOE_FMT_BF16: e = p3_fmt<MOE_FMT_BF16>(a, is, ss, s); break;
-    case MOE_FMT_Q2K: e = p3_fmt<MOE_FMT_Q2K>(a, is, ss, s); break;
-    case MOE_FMT_VQ2: e = p3_fmt<MOE_FMT_VQ2>(a, is, ss, s); break;
-    default: e = p3_fmt<MOE_FMT_MXFP4>(a, is, ss, s); break;
+    case MOE_FMT_BF16: e = p3_fmt<MOE_FMT_BF16>(a, is, s); break;
+    case MOE_FMT_Q2K: e = p3_fmt<MOE_FMT_Q2K>(a, is, s); break;
+    case MOE_FMT_VQ2: e = p3_fmt<MOE_FMT_VQ2>(a, is, s); break;
+    default: e = p3_fmt<MOE_FMT_MXFP4>(a, is, s); break;
   }
   return e;
 }

@@ -163,6 +163,7 @@ struct DecodeArgs {
   int a_mode;                // how a is stored (set by launch_decode1)
   int32_t *topk_idx;         // [k]
   float *topk_w;             // [k]
+  float *shared_y;           // [H] shared expert output (written by p2)
   float *out;                // [H]
   uint16_t *out_bf16;        // optional [H]
   int nb_router, nb_shared_gu, nb_routed, tiles_per_expert;
