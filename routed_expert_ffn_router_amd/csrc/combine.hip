@@ -42,8 +42,8 @@ hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_
                           const float *w, const float *shared_y, float *out, uint16_t *out_bf16,
                           hipStream_t s) {
   dim3 grid((H / 4 + 255) / 256, T);
-  launch(k_combine, dim3(grid), dim3(256), s, T, H, k, y_rows, slot_pos, w, shared_y, out, out_bf16);
-  return hipGetLastError();
+  return launch(k_combine, dim3(grid), dim3(256), s, T, H, k, y_rows, slot_pos, w, shared_y, out,
+                out_bf16);
 }
 
 // ---------------------------------------------------------------------------
@@ -86,8 +86,7 @@ hipError_t launch_dequant(const WView &w, int expert, int64_t w0, int64_t count,
                           hipStream_t s) {
   int64_t blocks = (count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  launch(k_dequant, dim3((unsigned)blocks), dim3(256), s, w, expert, w0, count, out);
-  return hipGetLastError();
+  return launch(k_dequant, dim3((unsigned)blocks), dim3(256), s, w, expert, w0, count, out);
 }
 
 }  // namespace moe

@@ -294,11 +294,9 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
   if (a.nb_router + a.nb_shared_gu > 0) {
     mark(mark_ctx, "decode_p1");
     const int g1 = max(a.nb_router, a.nb_shared_gu);
-    if (hs == 4)
-      launch(k_dec_p1<4>, dim3(g1), dim3(kP1Threads), s, a);
-    else
-      launch(k_dec_p1<2>, dim3(g1), dim3(kP1Threads), s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = hs == 4 ? launch(k_dec_p1<4>, dim3(g1), dim3(kP1Threads), s, a)
+                : launch(k_dec_p1<2>, dim3(g1), dim3(kP1Threads), s, a);
+    if (e != hipSuccess) return e;
   }
   mark(mark_ctx, "decode_p2");
   switch (a.gate.fmt) {

@@ -603,8 +603,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_skinny(SkinnyArgs p) {
 // stages), output columns a multiple of the block's (128 a columns, 256 down)
 hipError_t launch_tile_list(int E, int n_dense, int bm, const int32_t *offsets, int32_t *tiles,
                             hipStream_t s) {
-  launch(k_tile_list, dim3(1), dim3(1024), s, offsets ? E : 0, n_dense, bm, offsets, tiles);
-  return hipGetLastError();
+  return launch(k_tile_list, dim3(1), dim3(1024), s, offsets ? E : 0, n_dense, bm, offsets, tiles);
 }
 
 bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
@@ -619,9 +618,8 @@ template <int MODE, int BM>
 hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s) {
 #define MOE_GEMM_CASE(F, O)                                                              \
   if (fmt == F && op == O) {                                                             \
-    launch(k_gemm<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),             \
-           dim3(kGemmThreads), s, a);                                                    \
-    return hipGetLastError();                                                            \
+    return launch(k_gemm<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),      \
+                  dim3(kGemmThreads), s, a);                                             \
   }
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpBF16)
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpF16)
@@ -646,8 +644,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   const int E = offsets ? gate.E : 0;
   const int max_tiles = ((n_rows + BM - 1) / BM + E + 7) / 8 * 8;
   if (mark) mark(mark_ctx, names[0]);
-  launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, BM, offsets, tiles);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, BM, offsets, tiles);
   if (err != hipSuccess) return err;
 
   GemmArgs g{};
@@ -678,13 +675,11 @@ static hipError_t skinny_mb(const WView &gate, const WView &up, const WView &dow
   SkinnyArgs g{T, H, I, reinterpret_cast<const uint16_t *>(gate.data),
                reinterpret_cast<const uint16_t *>(up.data), x, a16, nullptr};
   if (mark) mark(mark_ctx, names[1]);
-  launch(k_skinny<kModeGateUp, MB>, dim3(I / 16), dim3(64 * kSkWaves), s, g);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch(k_skinny<kModeGateUp, MB>, dim3(I / 16), dim3(64 * kSkWaves), s, g);
   if (err != hipSuccess) return err;
   SkinnyArgs d{T, I, H, reinterpret_cast<const uint16_t *>(down.data), nullptr, a16, nullptr, y};
   if (mark) mark(mark_ctx, names[2]);
-  launch(k_skinny<kModeDown, MB>, dim3(H / 16), dim3(64 * kSkWaves), s, d);
-  return hipGetLastError();
+  return launch(k_skinny<kModeDown, MB>, dim3(H / 16), dim3(64 * kSkWaves), s, d);
 }
 
 bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down) {

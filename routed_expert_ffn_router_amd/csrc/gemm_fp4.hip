@@ -349,18 +349,17 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   g.tiles = tiles, g.out_q = aq, g.out_s = as;
   g.weight_major = !offsets && (I / a8_block_cols<kModeGateUp>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
-  launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
-         dim3(kA8Threads), s, g);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  err = launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
+               dim3(kA8Threads), s, g);
+  if (err != hipSuccess) return err;
 
   A8Args d{};
   d.K = I, d.N = H, d.w0 = down, d.w1 = down, d.aq = aq, d.as = as, d.a_rows = n_rows;
   d.tiles = tiles, d.y_out = y;
   d.weight_major = !offsets && (H / a8_block_cols<kModeDown>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[2]);
-  launch(k_gemm_a8<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
-         dim3(kA8Threads), s, d);
-  return hipGetLastError();
+  return launch(k_gemm_a8<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
+                dim3(kA8Threads), s, d);
 }
 
 }  // namespace
@@ -381,8 +380,8 @@ hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, 
   uint8_t *as = aq + up256((size_t)n_rows * I);
   if (mark) mark(mark_ctx, names[3]);
   const long n8 = (long)T * (H / 8);
-  launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, T, H, x, xq, xs);
-  hipError_t err = hipGetLastError();
+  hipError_t err =
+      launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, T, H, x, xq, xs);
   if (err != hipSuccess) return err;
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
   if (n_rows >= 32 * active)
@@ -398,8 +397,7 @@ hipError_t launch_mx8_quant(int rows, int K, const uint16_t *x, uint8_t *q, uint
   if (K % 32 || rows < 0) return hipErrorInvalidValue;
   if (rows == 0) return hipSuccess;
   const long n8 = (long)rows * (K / 8);
-  launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, rows, K, x, q, sc);
-  return hipGetLastError();
+  return launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, rows, K, x, q, sc);
 }
 
 }  // namespace moe

@@ -92,10 +92,8 @@ hipError_t gateup_inst(const GateUpArgs &a, int max_active, int ntok_hint, hipSt
   constexpr int RPB = 4 * ST * (64 / LPR);
   dim3 grid((a.I + RPB - 1) / RPB, a.plan ? max_active : 1);
   if (ntok_hint >= 4)
-    launch(k_gateup<FMT, SPL, LPR, ST, 4>, dim3(grid), dim3(256), s, a);
-  else
-    launch(k_gateup<FMT, SPL, LPR, ST, 1>, dim3(grid), dim3(256), s, a);
-  return hipGetLastError();
+    return launch(k_gateup<FMT, SPL, LPR, ST, 4>, dim3(grid), dim3(256), s, a);
+  return launch(k_gateup<FMT, SPL, LPR, ST, 1>, dim3(grid), dim3(256), s, a);
 }
 
 template <int FMT, int SPL, int LPR>
@@ -104,10 +102,8 @@ hipError_t down_inst(const DownArgs &a, int max_active, int ntok_hint, hipStream
   constexpr int RPB = 4 * ST * (64 / LPR);
   dim3 grid((a.H + RPB - 1) / RPB, a.plan ? max_active : 1);
   if (ntok_hint >= 4)
-    launch(k_down<FMT, SPL, LPR, ST, 4>, dim3(grid), dim3(256), s, a);
-  else
-    launch(k_down<FMT, SPL, LPR, ST, 1>, dim3(grid), dim3(256), s, a);
-  return hipGetLastError();
+    return launch(k_down<FMT, SPL, LPR, ST, 4>, dim3(grid), dim3(256), s, a);
+  return launch(k_down<FMT, SPL, LPR, ST, 1>, dim3(grid), dim3(256), s, a);
 }
 
 template <int FMT>

@@ -23,7 +23,8 @@ inline void kernel_arg_ptrs(std::tuple<P...> &t, void **out, std::index_sequence
   ((out[I] = static_cast<void *>(&std::get<I>(t))), ...);
 }
 
-// every libmoe kernel is launched through here
+// every libmoe kernel is launched through here; returns the launch's error,
+// else any error the thread had pending
 template <typename... P, typename... A>
 inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A &&...a) {
   static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
@@ -32,8 +33,10 @@ inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
   kernel_arg_ptrs(args, ptrs, std::index_sequence_for<P...>{});
   hipEvent_t ts, te;
   timer_take(&ts, &te);
-  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s, ts,
-                            te, 0);
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block,
+                                          ptrs, 0, s, ts, te, 0);
+  const hipError_t pending = hipGetLastError();  // also clears the thread's error state
+  return e != hipSuccess ? e : pending;
 }
 
 // A projection as the kernels see it.

@@ -155,14 +155,13 @@ hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const ui
   if (T <= 8) {
     const int waves = T * E;
     const int blocks = (waves + 3) / 4;
-    launch(k_router_gemv, dim3(blocks), dim3(256), s, T, H, E, x, wr, logits);
-  } else if (E % 64 == 0 && H % 32 == 0) {
-    launch(k_router_mfma, dim3(E / 64, (T + 31) / 32), dim3(256), s, T, H, E, x, wr, logits);
-  } else {
-    dim3 grid((E + 63) / 64, (T + 31) / 32);
-    launch(k_router_gemm, dim3(grid), dim3(256), s, T, H, E, x, wr, logits);
+    return launch(k_router_gemv, dim3(blocks), dim3(256), s, T, H, E, x, wr, logits);
   }
-  return hipGetLastError();
+  if (E % 64 == 0 && H % 32 == 0)
+    return launch(k_router_mfma, dim3(E / 64, (T + 31) / 32), dim3(256), s, T, H, E, x, wr,
+                  logits);
+  dim3 grid((E + 63) / 64, (T + 31) / 32);
+  return launch(k_router_gemm, dim3(grid), dim3(256), s, T, H, E, x, wr, logits);
 }
 
 // ----------------------------------------------------------------------------
@@ -276,13 +275,11 @@ hipError_t launch_select(int mode, int T, int E, int k, const float *logits,
                          const int64_t *token_ids, int32_t *idx, float *w, int32_t *offsets,
                          int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos,
                          float *row_w, int32_t *plan, hipStream_t s) {
-  if (sorted_token) {
-    launch(k_select_plan, dim3(1), dim3(1024), s, mode, T, E, k, logits, token_ids, idx, w, offsets,
-                                     sorted_token, sorted_slot, slot_pos, row_w, plan);
-  } else {
-    launch(k_select, dim3((T + 3) / 4), dim3(256), s, mode, T, E, k, logits, token_ids, idx, w);
-  }
-  return hipGetLastError();
+  if (sorted_token)
+    return launch(k_select_plan, dim3(1), dim3(1024), s, mode, T, E, k, logits, token_ids, idx, w,
+                  offsets, sorted_token, sorted_slot, slot_pos, row_w, plan);
+  return launch(k_select, dim3((T + 3) / 4), dim3(256), s, mode, T, E, k, logits, token_ids, idx,
+                w);
 }
 
 // ----------------------------------------------------------------------------
@@ -361,13 +358,14 @@ hipError_t launch_dispatch(int T, int E, int k, const int32_t *idx, int32_t *off
   const int nchunks = (n + kChunk - 1) / kChunk;
   int32_t *counts = static_cast<int32_t *>(ws);
   if (mark) mark(mark_ctx, "dispatch_counts");
-  launch(k_chunk_counts, dim3(nchunks), dim3(kChunk), s, n, E, idx, counts);
+  hipError_t err = launch(k_chunk_counts, dim3(nchunks), dim3(kChunk), s, n, E, idx, counts);
+  if (err != hipSuccess) return err;
   if (mark) mark(mark_ctx, "dispatch_scan");
-  launch(k_chunk_scan, dim3(1), dim3(1024), s, n, nchunks, E, counts, offsets);
+  err = launch(k_chunk_scan, dim3(1), dim3(1024), s, n, nchunks, E, counts, offsets);
+  if (err != hipSuccess) return err;
   if (mark) mark(mark_ctx, "dispatch_scatter");
-  launch(k_chunk_scatter, dim3(nchunks), dim3(kChunk), s, n, E, k, idx, counts, sorted_token,
-         sorted_slot, slot_pos);
-  return hipGetLastError();
+  return launch(k_chunk_scatter, dim3(nchunks), dim3(kChunk), s, n, E, k, idx, counts,
+                sorted_token, sorted_slot, slot_pos);
 }
 
 // compact plan from offsets: one 1024-thread block (E <= 1024)
@@ -387,8 +385,7 @@ __global__ __launch_bounds__(1024) void k_plan_from_offsets(int E, const int32_t
 }
 
 hipError_t launch_plan_from_offsets(int E, const int32_t *offsets, int32_t *plan, hipStream_t s) {
-  launch(k_plan_from_offsets, dim3(1), dim3(1024), s, E, offsets, plan);
-  return hipGetLastError();
+  return launch(k_plan_from_offsets, dim3(1), dim3(1024), s, E, offsets, plan);
 }
 
 }  // namespace moe
