@@ -71,13 +71,13 @@ KERNEL_OF = {"decode_p1": "k_dec_p1", "decode_p2": "k_dec_p2", "decode_p3": "k_d
              "combine": "k_combine", "select": "k_select", "select_plan": "k_select_plan",
              "routed_gateup": "k_gateup", "routed_down": "k_down", "shared_gateup": "k_gateup",
              "shared_down": "k_down", "a8_gemm_gateup": "k_gemm_a8<0", "a8_gemm_down": "k_gemm_a8<1",
-             "act_quant": "k_mx8_quant"}
+             "act_quant": "k_mx8_quant", "tokens_f16": "k_tokens_f16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 # kernel symbol substring -> the source file it is built from
 SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm_a8", "gemm_fp4.hip"), ("k_mx8", "gemm_fp4.hip"),
-             ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"),
+             ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"), ("k_tokens_f16", "gemm.hip"),
              ("k_skinny", "gemm.hip"), ("k_router", "route.hip"), ("k_select", "route.hip"),
              ("k_chunk", "route.hip"), ("k_plan", "route.hip"), ("k_gateup", "gemv.hip"),
              ("k_down", "gemv.hip"), ("k_dequant", "gemv.hip"), ("k_combine", "combine.hip"))
@@ -227,6 +227,8 @@ def kernel_cost(name, L, T, U, n):
         "gemm_down": (U * dn + n * I * 2 + n * H * 4, 2 * n * H * I),
         # MX-FP8 activations (1 byte + a scale byte per 32) on the FP4 matrix cores
         "act_quant": (xb + T * H + T * H // 32, 0),
+        "tokens_f16": (2 * xb, 0),
+        "shared_tokens_f16": (2 * xb, 0),
         "a8_gemm_gateup": (U * gu + T * H + T * H // 32 + n * I + n * I // 32, 4 * n * I * H),
         "a8_gemm_down": (U * dn + n * I + n * I // 32 + n * H * 4, 2 * n * H * I),
         "combine": (n * H * 4 + 2 * T * H * 4 + n * 8, 2 * n * H),

@@ -140,15 +140,17 @@ WView bf16_view(const uint16_t *p, int N, int K) {
 // expert FFN workspace and sequence (shared by moe_expert_ffn and moe_forward)
 // ---------------------------------------------------------------------------
 
-const char *const kRoutedGemmNames[3] = {"tile_list", "gemm_gateup", "gemm_down"};
-const char *const kSharedGemmNames[3] = {"shared_tile_list", "shared_gemm_gateup",
-                                         "shared_gemm_down"};
+const char *const kRoutedGemmNames[4] = {"tile_list", "gemm_gateup", "gemm_down",
+                                         "tokens_f16"};
+const char *const kSharedGemmNames[4] = {"shared_tile_list", "shared_gemm_gateup",
+                                         "shared_gemm_down", "shared_tokens_f16"};
 const char *const kA8Names[4] = {"tile_list", "a8_gemm_gateup", "a8_gemm_down", "act_quant"};
 
 struct FfnBufs {
   int32_t *plan;
   float *a;        // fp32 SwiGLU output of the GEMV path; fp16 on the GEMM path
   int32_t *tiles;  // GEMM tile list
+  uint16_t *x16;   // GEMM path: the tokens as fp16 operands
   void *a8;        // MX-FP8 tokens and SwiGLU output (MOE_ACT_MXFP8)
 };
 
@@ -157,6 +159,7 @@ FfnBufs carve_ffn(Carver &c, int T, int n_rows, int E, int H, int I, bool dense,
   b.plan = dense ? nullptr : c.take<int32_t>(plan_ints(std::min(E, std::max(n_rows, 1))));
   b.a = c.take<float>((size_t)std::max(n_rows, 1) * I);
   b.tiles = c.take<int32_t>(gemm_tile_ints(std::max(n_rows, 1), dense ? 0 : E));
+  b.x16 = c.take<uint16_t>((size_t)std::max(T, 1) * H);
   if (act == MOE_ACT_MXFP8) b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, std::max(n_rows, 1)));
   return b;
 }
@@ -191,7 +194,7 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
                      "skinny ffn");
   if (use_gemm(T, H, I, g.E, n_rows, !offsets, g.fmt, d.fmt))
     return hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
-                                     reinterpret_cast<uint16_t *>(b.a), y, s, mark_cb, &m,
+                                     reinterpret_cast<uint16_t *>(b.a), b.x16, y, s, mark_cb, &m,
                                      kRoutedGemmNames),
                      "gemm ffn");
   if (!offsets) {
@@ -224,6 +227,7 @@ struct FwdBufs {
   int32_t *tiles_sh;
   // small path
   int32_t *plan, *sorted_token, *slot_pos, *tiles;
+  uint16_t *x16;
   void *a8;
   float *row_w, *a, *y_rows;
   // large path
@@ -266,6 +270,7 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.y_rows = c.take<float>(n * H);
     b.offsets = c.take<int32_t>(E + 1);
     b.tiles = c.take<int32_t>(gemm_tile_ints((int)n, E));
+    b.x16 = c.take<uint16_t>((size_t)T * H);
     if (L->act_fmt == MOE_ACT_MXFP8) b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, (int)n));
   } else {
     b.offsets = c.take<int32_t>(E + 1);
@@ -499,7 +504,7 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
                         "shared skinny"));
     } else if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
       MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
-                                        b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh),
+                                        b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh), nullptr,
                                         b.shared_y, s, mark_cb, &mk, kSharedGemmNames),
                         "shared gemm"));
     } else {
@@ -525,8 +530,8 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     } else if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt)) {
       // several tokens: every selected expert's weights once, all its rows per load
       MOE_TRY(hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n,
-                                        b.tiles, reinterpret_cast<uint16_t *>(b.a), b.y_rows, s,
-                                        mark_cb, &mk, kRoutedGemmNames),
+                                        b.tiles, reinterpret_cast<uint16_t *>(b.a), b.x16,
+                                        b.y_rows, s, mark_cb, &mk, kRoutedGemmNames),
                         "gemm ffn"));
     } else {
       const int max_active = std::min(E, n);

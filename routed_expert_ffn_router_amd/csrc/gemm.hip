@@ -101,7 +101,7 @@ __global__ __launch_bounds__(1024) void k_tile_list(int E, int n_dense, int bm,
 struct GemmArgs {
   int K, N;                  // reduction length; columns of the layer's output (I or H)
   WView w0, w1;              // gate and up, or down (w0 == w1)
-  const uint16_t *x;         // gate/up: bf16 tokens [T][K]
+  const uint16_t *x;         // gate/up: tokens [T][K] in the operand type (bf16 or fp16)
   const int32_t *row_token;  // gate/up: token of each bucket row (null: the row itself)
   const uint16_t *a16;       // down: fp16 SwiGLU output [n_rows][K]
   int a_rows;                // rows of x (gate/up: T) or of a16 (down: n_rows)
@@ -238,7 +238,7 @@ struct BStageBf16 {
   }
 };
 
-// A stage: BM rows x 64 LDS columns; thread t stages row t / (256 / BM) and
+// A stage (already in the operand type): BM rows x 64 LDS columns; thread t stages row t / (256 / BM) and
 // the BM / 4 LDS columns from acol.  LDS column c of stage it holds
 // k = kb(it) + 64 (c / 16) + c % 16 with kb(it) = 256 (it / 4) + 16 (it % 4),
 // so a thread's columns are one run of 4 (BM 16) or runs of 16 (BM 64, 128)
@@ -263,16 +263,13 @@ struct AStage {
     }
   }
   __device__ __forceinline__ void store(uint32_t *dst) const {
-    uint32_t o[kDw];
-#pragma unroll
-    for (int i = 0; i < kDw; i++)
-      o[i] = (MODE == kModeGateUp && OP == kOpF16) ? bf16x2_to_f16x2(raw[i]) : raw[i];
     if constexpr (kDw == 2) {
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(raw[0], raw[1]);
     } else {
       uint4 *d4 = reinterpret_cast<uint4 *>(dst);
 #pragma unroll
-      for (int i = 0; i < kDw / 4; i++) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+      for (int i = 0; i < kDw / 4; i++)
+        d4[i] = make_uint4(raw[4 * i], raw[4 * i + 1], raw[4 * i + 2], raw[4 * i + 3]);
     }
   }
 };
@@ -599,6 +596,18 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_skinny(SkinnyArgs p) {
 // host
 // ---------------------------------------------------------------------------
 
+// bf16 tokens -> fp16 operands (round to nearest even; exact for every bf16
+// value inside the fp16 normal range), once per call instead of once per
+// column block of the gate/up GEMM
+__global__ __launch_bounds__(256) void k_tokens_f16(long n8, const uint4 *__restrict__ x,
+                                                     uint4 *__restrict__ x16) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = x[i];
+  x16[i] = make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+                      bf16x2_to_f16x2(v.w));
+}
+
 // K a multiple of 256 (whole Q2K / VQ2 groups; a whole number of register
 // stages), output columns a multiple of the block's (128 a columns, 256 down)
 hipError_t launch_tile_list(int E, int n_dense, int bm, const int32_t *offsets, int32_t *tiles,
@@ -638,14 +647,23 @@ int gateup_op(int fmt) {
 template <int BM>
 hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H, int I, int T,
                    const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
-                   int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
-                   void (*mark)(void *, const char *), void *mark_ctx,
-                   const char *const names[3]) {
+                   int n_rows, int32_t *tiles, uint16_t *a16, uint16_t *x16, float *y,
+                   hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
+                   const char *const names[4]) {
   const int E = offsets ? gate.E : 0;
   const int max_tiles = ((n_rows + BM - 1) / BM + E + 7) / 8 * 8;
   if (mark) mark(mark_ctx, names[0]);
   hipError_t err = launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, BM, offsets, tiles);
   if (err != hipSuccess) return err;
+
+  if (gateup_op(gate.fmt) == kOpF16) {
+    if (mark) mark(mark_ctx, names[3]);
+    const long n8 = (long)T * H / 8;  // H % 256 == 0
+    err = launch(k_tokens_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, n8,
+                 reinterpret_cast<const uint4 *>(x), reinterpret_cast<uint4 *>(x16));
+    if (err != hipSuccess) return err;
+    x = x16;
+  }
 
   GemmArgs g{};
   g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x, g.a_rows = T;
@@ -671,7 +689,7 @@ template <int MB>
 static hipError_t skinny_mb(const WView &gate, const WView &up, const WView &down, int H, int I,
                             int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
                             void (*mark)(void *, const char *), void *mark_ctx,
-                            const char *const names[3]) {
+                            const char *const names[4]) {
   SkinnyArgs g{T, H, I, reinterpret_cast<const uint16_t *>(gate.data),
                reinterpret_cast<const uint16_t *>(up.data), x, a16, nullptr};
   if (mark) mark(mark_ctx, names[1]);
@@ -690,7 +708,7 @@ bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down)
 hipError_t launch_skinny_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                              int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
                              void (*mark)(void *, const char *), void *mark_ctx,
-                             const char *const names[3]) {
+                             const char *const names[4]) {
   if (!skinny_supported(H, I, T, gate, down)) return hipErrorInvalidValue;
   if (T <= 16) return skinny_mb<1>(gate, up, down, H, I, T, x, a16, y, s, mark, mark_ctx, names);
   if (T <= 32) return skinny_mb<2>(gate, up, down, H, I, T, x, a16, y, s, mark, mark_ctx, names);
@@ -700,20 +718,22 @@ hipError_t launch_skinny_ffn(const WView &gate, const WView &up, const WView &do
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                            int T, const uint16_t *x, const int32_t *offsets,
                            const int32_t *sorted_token, int n_rows, int32_t *tiles, uint16_t *a16,
-                           float *y, hipStream_t s, void (*mark)(void *, const char *),
-                           void *mark_ctx, const char *const names[3]) {
+                           uint16_t *x16, float *y, hipStream_t s,
+                           void (*mark)(void *, const char *), void *mark_ctx,
+                           const char *const names[4]) {
   if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
+  if (gateup_op(gate.fmt) == kOpF16 && !x16) return hipErrorInvalidValue;
   // rows per tile: 128 once the active experts average 96 rows or more (each
   // weight read for more rows), 64 from 32 rows, else 16
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
   if (n_rows >= 96 * active)
-    return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y,
-                        s, mark, mark_ctx, names);
+    return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16,
+                        x16, y, s, mark, mark_ctx, names);
   if (n_rows >= 32 * active)
-    return gemm_bm<64>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y, s,
-                       mark, mark_ctx, names);
-  return gemm_bm<16>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, y, s,
-                     mark, mark_ctx, names);
+    return gemm_bm<64>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16,
+                       y, s, mark, mark_ctx, names);
+  return gemm_bm<16>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16, y,
+                     s, mark, mark_ctx, names);
 }
 
 }  // namespace moe

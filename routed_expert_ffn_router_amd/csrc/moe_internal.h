@@ -114,14 +114,16 @@ hipError_t launch_down_gemv(const WView &down, int H, int I, const float *a,
 // prefill grouped GEMMs (gemm.hip) --------------------------------------------
 // Whole expert FFN on the matrix cores: y[r] = down_e . SwiGLU(gate_e, up_e; x[tok[r]])
 // for every bucket row r (offsets null: one dense expert over rows [0, n_rows = T)).
-// tiles: gemm_tile_ints(n_rows, offsets ? E : 0) ints; a16: fp16 [n_rows][I].
+// tiles: gemm_tile_ints(n_rows, offsets ? E : 0) ints; a16: fp16 [n_rows][I];
+// x16: fp16 [T][H], the tokens converted for fp16 gate/up operands (VQ2, Q2K
+// gate), may be null otherwise.  names: tile list, gate/up, down, conversion.
 bool gemm_supported(int H, int I, int fmt_gate, int fmt_down);
 size_t gemm_tile_ints(int n_rows, int E);
 hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                            int T, const uint16_t *x, const int32_t *offsets, const int32_t *sorted_token,
-                           int n_rows, int32_t *tiles, uint16_t *a16, float *y, hipStream_t s,
-                           void (*mark)(void *, const char *), void *mark_ctx,
-                           const char *const names[3]);
+                           int n_rows, int32_t *tiles, uint16_t *a16, uint16_t *x16, float *y,
+                           hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
+                           const char *const names[4]);
 
 // tile list of the grouped GEMMs: tiles of bm rows over the buckets
 // (offsets [E+1]), or over rows [0, n_dense) of one dense expert (offsets null)
@@ -147,7 +149,7 @@ bool skinny_supported(int H, int I, int T, const WView &gate, const WView &down)
 hipError_t launch_skinny_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                              int T, const uint16_t *x, uint16_t *a16, float *y, hipStream_t s,
                              void (*mark)(void *, const char *), void *mark_ctx,
-                             const char *const names[3]);
+                             const char *const names[4]);
 
 // fused batch-1 decode (decode.hip) ------------------------------------------
 struct DecodeArgs {
