@@ -119,26 +119,35 @@ __global__ __launch_bounds__(256) void k_router_mfma(int T, int H, int E,
   const uint4 *wb1 = reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + 16 + r) * H + 8 * g);
   f64x4_t c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
   const int n = H / 32;
-  uint4 a = xa[0], b0 = wb0[0], b1 = wb1[0];
-  for (int i = 0; i < n; i++) {
-    uint4 an = a, b0n = b0, b1n = b1;
-    if (i + 1 < n) {
-      an = xa[4 * (i + 1)];
-      b0n = wb0[4 * (i + 1)];
-      b1n = wb1[4 * (i + 1)];
-    }
-    const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t bv0[4] = {b0.x, b0.y, b0.z, b0.w};
-    const uint32_t bv1[4] = {b1.x, b1.y, b1.z, b1.w};
+  // a ring of kP steps in flight: one step of MFMAs alone is far shorter than
+  // a memory round trip, and a block holds one wave per SIMD
+  constexpr int kP = 4;
+  uint4 a[kP], b0[kP], b1[kP];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const double alo = bf16_lo(av[j]), ahi = bf16_hi(av[j]);
-      c0 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv0[j]), c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv1[j]), c1, 0, 0, 0);
-      d0 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv0[j]), d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv1[j]), d1, 0, 0, 0);
+  for (int u = 0; u < kP; u++) {
+    const int i = min(u, n - 1);
+    a[u] = xa[4 * i], b0[u] = wb0[4 * i], b1[u] = wb1[4 * i];
+  }
+  for (int i0 = 0; i0 < n; i0 += kP) {
+#pragma unroll
+    for (int u = 0; u < kP; u++) {
+      if (i0 + u < n) {
+        const uint32_t av[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+        const uint32_t bv0[4] = {b0[u].x, b0[u].y, b0[u].z, b0[u].w};
+        const uint32_t bv1[4] = {b1[u].x, b1[u].y, b1[u].z, b1[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const double alo = bf16_lo(av[j]), ahi = bf16_hi(av[j]);
+          c0 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv0[j]), c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f64_16x16x4f64(alo, (double)bf16_lo(bv1[j]), c1, 0, 0, 0);
+          d0 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv0[j]), d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f64_16x16x4f64(ahi, (double)bf16_hi(bv1[j]), d1, 0, 0, 0);
+        }
+      }
+      // refill the slot (past the end: the last step again, never used)
+      const int i = min(i0 + u + kP, n - 1);
+      a[u] = xa[4 * i], b0[u] = wb0[4 * i], b1[u] = wb1[4 * i];
     }
-    a = an, b0 = b0n, b1 = b1n;
   }
 #pragma unroll
   for (int q = 0; q < 4; q++) {
@@ -299,25 +308,39 @@ __global__ __launch_bounds__(kChunk) void k_chunk_counts(int n, int E, const int
   for (int e = threadIdx.x; e < E; e += kChunk) counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// one 1024-thread block: thread e walks the chunks of expert e; then a scan
-// over experts turns per-chunk counts into global bucket starts
+// one 1024-thread block: thread e sums the chunk counts of expert e, a scan
+// over experts gives the bucket starts, then thread e rewrites its chunks'
+// counts as global starts.  Counts are read kBatch at a time before any
+// store, so each pass waits for memory nchunks / kBatch times, not nchunks.
 __global__ __launch_bounds__(1024) void k_chunk_scan(int n, int nchunks, int E,
                                                       int32_t *__restrict__ counts,
                                                       int32_t *__restrict__ offsets) {
+  constexpr int kBatch = 16;
   __shared__ int s_tmp[16];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E)
-    for (int b = 0; b < nchunks; b++) {
-      const int c = counts[(size_t)b * E + e];
-      counts[(size_t)b * E + e] = tot;
-      tot += c;
+    for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+#pragma unroll
+      for (int j = 0; j < kBatch; j++)
+        tot += b0 + j < nchunks ? counts[(size_t)(b0 + j) * E + e] : 0;
     }
   int total;
   const int off = block_excl_scan_1024(e < E ? tot : 0, s_tmp, &total);
   if (e < E) {
     offsets[e] = off;
-    for (int b = 0; b < nchunks; b++) counts[(size_t)b * E + e] += off;
+    int run = off;
+    for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; j++) c[j] = b0 + j < nchunks ? counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; j++)
+        if (b0 + j < nchunks) {
+          counts[(size_t)(b0 + j) * E + e] = run;
+          run += c[j];
+        }
+    }
   }
   if (e == 0) offsets[E] = n;
 }
