@@ -176,26 +176,34 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
     __syncthreads();
   }
   {
-    // rows whose loads are in flight per wave: eight when their raw bits fit
-    // in about 48 registers (not MXFP4's wider chunks), else four
+    // rows whose loads are in flight per wave: all of the block's rows when
+    // their raw bits fit in about 96 registers (the 2-bit formats), else four
     constexpr int kDw = DFMT == MOE_FMT_BF16 ? 8 * DSPL : DFMT == MOE_FMT_VQ2 ? 2 * DSPL : 3 * DSPL;
-    constexpr int PF = DFMT != MOE_FMT_MXFP4 && 48 / kDw >= 8 ? 8 : 4;
+    constexpr int PF = DFMT != MOE_FMT_MXFP4 && 96 / kDw >= kP3Rows ? kP3Rows : 4;
     const uint2 *cb = s_cb + (lane % kNCopy);
     float acc[kP3Rows];
 #pragma unroll
     for (int r = 0; r < kP3Rows; r++) acc[r] = 0.0f;
+    // the slot's activations do not depend on the choice: with the 2-bit
+    // formats they are requested first and travel alongside the expert index;
+    // MXFP4's wider rows go first instead
+    constexpr bool kAFirst = DFMT != MOE_FMT_MXFP4;
     for (int j = wave; j < p.k; j += kDecWaves) {
+      ADown<DFMT, DSPL, 64> av[1];
+      auto load_a = [&]() {
+        if constexpr (DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_BF16)
+          av[0].load_split(p.a_hi + (size_t)j * p.I, p.a_lo + (size_t)j * p.I, lane);
+        else
+          av[0].load(p.a + (size_t)j * p.I, lane);
+      };
+      if constexpr (kAFirst) load_a();
       const int e = __builtin_amdgcn_readfirstlane(p.topk_idx[j]);
       const float wj = __builtin_bit_cast(
           float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.topk_w[j])));
       Chunk<DFMT, DSPL, 64> c[PF];
 #pragma unroll
       for (int r = 0; r < PF; r++) c[r].load(p.down, e, min(row0 + r, p.H - 1), lane);
-      ADown<DFMT, DSPL, 64> av[1];
-      if constexpr (DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_BF16)
-        av[0].load_split(p.a_hi + (size_t)j * p.I, p.a_lo + (size_t)j * p.I, lane);
-      else
-        av[0].load(p.a + (size_t)j * p.I, lane);
+      if constexpr (!kAFirst) load_a();
 #pragma unroll
       for (int r = 0; r < kP3Rows; r++) {
         float y[1];
