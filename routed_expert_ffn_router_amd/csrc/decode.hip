@@ -108,13 +108,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int64_t tid0 = *(p.tid ? p.tid : reinterpret_cast<const int64_t *>(p.x));
   uint32_t cbw = 0;
   if constexpr (RFMT == MOE_FMT_VQ2) cbw = codebook_entry_load(p.gate.codebook);
-  // then this wave's shared down row gw (the wave's own, independent of the
-  // selection: it streams while the selection runs) and p1's SwiGLU output
-  const int gw = blockIdx.x * kDecWaves + wave;
-  Chunk<MOE_FMT_BF16, SSPL, 64> csh;
+  // then the shared down rows of waves 1..7 and p1's SwiGLU output: the
+  // block's rows 8 b + w (+ 8 nb ...) go to wave w, row 8 b + 0 to wave 1
+  // too, so that wave 0 only selects; they stream and are reduced while the
+  // selection runs
+  const int rb0 = blockIdx.x * kDecWaves;
+  Chunk<MOE_FMT_BF16, SSPL, 64> csh[2];
   ADown<MOE_FMT_BF16, SSPL, 64> ash[1];
-  if (p.Is) {
-    csh.load(p.sd, 0, min(gw, p.H - 1), lane);
+  if (p.Is && wave > 0) {
+    csh[0].load(p.sd, 0, min(rb0 + wave, p.H - 1), lane);
+    if (wave == 1) csh[1].load(p.sd, 0, min(rb0, p.H - 1), lane);
     ash[0].load_split(p.a_sh_hi, p.a_sh_lo, lane);
   }
   asm volatile("" ::"v"(cbw), "v"(lg.v[0]), "v"(lg.v[1]), "v"(lg.v[2]), "v"(lg.v[3]),
@@ -134,18 +137,27 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
         p.topk_w[lane] = w;
       }
     }
-  }
-  __syncthreads();
-  // the shared down rows gw, gw + 8 nb, ... (their data is in by now)
-  if (p.Is) {
-    for (int r = gw; r < p.H; r += gridDim.x * kDecWaves) {
-      if (r != gw) csh.load(p.sd, 0, r, lane);
+  } else if (p.Is) {
+    const int step = gridDim.x * kDecWaves;
+    for (int base = rb0; base < p.H; base += step) {
+      if (base != rb0) {
+        csh[0].load(p.sd, 0, min(base + wave, p.H - 1), lane);
+        if (wave == 1) csh[1].load(p.sd, 0, base, lane);
+      }
       float y[1];
-      csh.template dot_a<1>(ash, nullptr, y);
-      y[0] = wave_sum_f(y[0]);
-      if (lane == 0) p.shared_y[r] = y[0];
+      if (base + wave < p.H) {
+        csh[0].template dot_a<1>(ash, nullptr, y);
+        y[0] = wave_sum_f(y[0]);
+        if (lane == 0) p.shared_y[base + wave] = y[0];
+      }
+      if (wave == 1) {
+        csh[1].template dot_a<1>(ash, nullptr, y);
+        y[0] = wave_sum_f(y[0]);
+        if (lane == 0) p.shared_y[base] = y[0];
+      }
     }
   }
+  __syncthreads();
   constexpr int ST = steps_for<RFMT, RSPL>();
   const int j = blockIdx.x / p.tiles_per_expert, tile = blockIdx.x % p.tiles_per_expert;
   const int row_base = (tile * kDecWaves + wave) * ST;

@@ -279,6 +279,46 @@ def test_forward_mxfp4_decode(dev, mx, dmx, route):
     _forward_case(mx, dmx, dev, 9, 4, route=route)
 
 
+def _decode_select_cases(E):
+    """Logit rows for one-token selection edge cases (E >= 32)."""
+    rng = np.random.default_rng(77)
+    rows = []
+    rows.append(np.full(E, 0.5, np.float32))                 # all tie: 0..7
+    r = rng.standard_normal(E).astype(np.float32)
+    r[10:20] = r.max() + 1                                   # ten equal maxima
+    rows.append(r)
+    r = rng.standard_normal(E).astype(np.float32)
+    r[::3] = np.nan                                          # NaN ranks as -inf
+    rows.append(r)
+    r = np.full(E, -np.inf, np.float32)
+    r[[E - 1, 7, 130 % E, 64 % E, 3]] = [2.0, 1.0, 1.0, -0.0, 0.0]  # 5 finite, -0 ties +0
+    r[[11, 12]] = np.nan
+    rows.append(r)
+    r = rng.standard_normal(E).astype(np.float32)
+    r[[5, 69 % E, 133 % E, 197 % E]] = 9.0                   # one tie per lane slot
+    rows.append(r)
+    rows.append(-np.abs(rng.standard_normal(E)).astype(np.float32))
+    return rows
+
+
+def test_forward_decode_b1_selection_edges(dev, q2, dq2):
+    """One-token forward with given logits: the choices and weights equal the
+    oracle's selection and the batched moe_route's bit for bit, on ties,
+    NaNs, -inf, signed zeros and ties across lane slots."""
+    E = 256
+    x = t16(synth.gen_x(4096, 1, seed=9), dev)
+    for n, row in enumerate(_decode_select_cases(E)):
+        lg = row[None, :].copy()
+        lt = torch.from_numpy(lg).to(dev)
+        _, idx, w = moe.forward(dq2, x, logits_in=lt)
+        ref_idx, ref_w = oracle.select_topk(lg, 8)
+        assert np.array_equal(tnp(idx).reshape(1, 8), ref_idx), (n, tnp(idx), ref_idx)
+        np.testing.assert_allclose(tnp(w).reshape(1, 8), ref_w, rtol=1e-6, err_msg=str(n))
+        idx2, w2, _ = moe.route(None, None, 8, logits_in=lt)
+        assert np.array_equal(tnp(idx).reshape(1, 8), tnp(idx2)), n
+        assert bits_equal(tnp(w).reshape(1, 8), tnp(w2)), n
+
+
 def test_forward_deterministic(dev, q2, dq2):
     x = t16(synth.gen_x(4096, 16, seed=5), dev)
     a, _, _ = moe.forward(dq2, x)
