@@ -124,12 +124,15 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
                "v"((uint32_t)tid0), "v"((uint32_t)(tid0 >> 32)));
   if constexpr (RFMT == MOE_FMT_VQ2) codebook_entry_store<kDecThreads>(cbw, s_cb);
   if (wave == 0) {
+    // the selection is the block's critical path: its wave issues first
+    __builtin_amdgcn_s_setprio(3);
     int e;
     float w;
     if (small_e || p.mode == MOE_ROUTE_HASH)
       select_wave<4>(p.mode, p.E, p.k, lg, lsrc, tid0, &e, &w);
     else
       select_wave(p.mode, p.E, p.k, lsrc, 0, &e, &w);
+    __builtin_amdgcn_s_setprio(0);
     if (lane < p.k) {
       s_e[lane] = e;
       if (blockIdx.x == 0) {

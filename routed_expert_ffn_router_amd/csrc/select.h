@@ -68,6 +68,54 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
       my_e = e;
       my_l = r;
     }
+  } else if constexpr (NC == 4) {
+    // each lane sorts its four candidates once (value descending, index
+    // ascending on ties; NaN and absent candidates as -inf, absent ones after
+    // every present one by their index); a round then compares only the
+    // lanes' heads and the winner's lane pops its head
+    float v[4];
+    int id[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      id[i] = lane + 64 * i;
+      v[i] = id[i] < E ? order_val(lg.v[i]) : -INFINITY;
+    }
+    auto order = [&](int a, int b) {  // afterwards a comes before b
+      const bool sw = v[b] > v[a] || (v[b] == v[a] && id[b] < id[a]);
+      const float tv = v[a];
+      const int ti = id[a];
+      v[a] = sw ? v[b] : v[a];
+      id[a] = sw ? id[b] : id[a];
+      v[b] = sw ? tv : v[b];
+      id[b] = sw ? ti : id[b];
+    };
+    order(0, 1);
+    order(2, 3);
+    order(0, 2);
+    order(1, 3);
+    order(1, 2);
+    for (int j = 0; j < k; j++) {
+      const float m = wave_max_f(v[0]);
+      const uint64_t tied = __ballot(v[0] == m);
+      int e;
+      if ((tied & (tied - 1)) == 0)
+        e = __builtin_amdgcn_readlane(id[0], __builtin_ctzll(tied));
+      else  // several heads equal: the lowest index among them
+        e = wave_min_i(v[0] == m ? id[0] : 0x7FFFFFFF);
+      const bool pop = lane == (e & 63);
+      v[0] = pop ? v[1] : v[0];
+      id[0] = pop ? id[1] : id[0];
+      v[1] = pop ? v[2] : v[1];
+      id[1] = pop ? id[2] : id[1];
+      v[2] = pop ? v[3] : v[2];
+      id[2] = pop ? id[3] : id[2];
+      v[3] = pop ? -INFINITY : v[3];
+      id[3] = pop ? 0x7FFFFFFF : id[3];
+      if (lane == j) {
+        my_e = e;
+        my_l = m;  // already in selection-order form: NaN reads as -inf
+      }
+    }
   } else {
     float v[NC];
     uint32_t taken = 0;  // bit i: candidate lane + 64 i is taken or absent
