@@ -234,11 +234,57 @@ struct ADown<MOE_FMT_BF16, SPL, LPR> {
 
 // How a gate/up kernel stores the SwiGLU output a for the down kernel:
 // kAF32: fp32; kASplit: bf16 hi/lo arrays in natural order (bf16 down);
-// kASplitQ2K: bf16 hi/lo with each 16-value piece in Q2K pair order.
-constexpr int kAF32 = 0, kASplit = 1, kASplitQ2K = 2;
+// kASplitQ2K: bf16 hi/lo with each 16-value piece in Q2K pair order;
+// kAF16Q2K: fp16 (one array), each 16-value piece in the order of
+// ADownQ2K16's pairs.
+constexpr int kAF32 = 0, kASplit = 1, kASplitQ2K = 2, kAF16Q2K = 3;
 __device__ __forceinline__ int q2k_pair_pos(int i) {
   return (i & ~15) | ((i & 7) << 1) | ((i >> 3) & 1);
 }
+// value 4b + r of a piece sits at 4b + 2(r & 1) + (r >> 1): the pairs are
+// (a[4b], a[4b+2]) and (a[4b+1], a[4b+3])
+__device__ __forceinline__ int q2k16_pos(int i) {
+  return (i & ~3) | ((i & 1) << 1) | ((i >> 1) & 1);
+}
+
+// the two 2-bit codes held as E2M1 nibbles in byte b of w, as an exact fp16
+// pair (E2M1 codes 0..3 are 0, 0.5, 1, 1.5; the scale 2 makes them 0..3)
+__device__ __forceinline__ uint32_t q2_pair(uint32_t w, int b) {
+  switch (b) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 3));
+  }
+}
+
+// Q2K down against fp16 activations: per piece the 8 pairs in q2k16_pos
+// order and the piece's sum (fp32)
+template <int SPL, int LPR>
+struct ADownQ2K16 {
+  uint32_t h[SPL][8];
+  float sum[SPL];
+  __device__ __forceinline__ void load(const uint16_t *row, int kl) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(row, 0x7FFFFFFF);
+#pragma unroll
+    for (int i = 0; i < SPL; i++) {
+      const uint32_t vo = 2u * (uint32_t)piece_k<LPR>(kl, i);
+      const u32x4_t a0 = buf_u128(r, vo, 0), a1 = buf_u128(r, vo + 16, 0);
+      h[i][0] = a0.x, h[i][1] = a0.y, h[i][2] = a0.z, h[i][3] = a0.w;
+      h[i][4] = a1.x, h[i][5] = a1.y, h[i][6] = a1.z, h[i][7] = a1.w;
+    }
+  }
+  // the piece sums, once the pairs are in
+  __device__ __forceinline__ void sums() {
+#pragma unroll
+    for (int i = 0; i < SPL; i++) {
+      float s = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 8; m++) s = dot2_f16(h[i][m], 0x3C003C00u, s);
+      sum[i] = s;
+    }
+  }
+};
 
 // bf16 pairs of token `tok`'s pieces
 template <int SPL, int LPR>
@@ -394,6 +440,26 @@ struct Chunk<MOE_FMT_Q2K, SPL, LPR> {
         out[t] = fmaf(ds, sxq, fmaf(-ms, sx, out[t]));
       }
     }
+  }
+  // against fp16 activations: each code widened to an E2M1 nibble (q reads
+  // as q/2) and converted with the scale 2, so the pairs hold q exactly;
+  // then d sc sum(a q) - dmin m sum(a) per sub-block
+  __device__ __forceinline__ float dot_a16(const ADownQ2K16<SPL, LPR> &a) const {
+    float out = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPL; i++) {
+      const float d = f16_bits_to_f32(dm[i] & 0xFFFFu), dmin = f16_bits_to_f32(dm[i] >> 16);
+      const float ds = d * (float)(sc[i] & 15u), ms = dmin * (float)(sc[i] >> 4);
+      const uint32_t nl = qs[i] & 0x33333333u, nh = (qs[i] >> 2) & 0x33333333u;
+      float acc = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        acc = dot2_f16(a.h[i][2 * b], q2_pair(nl, b), acc);
+        acc = dot2_f16(a.h[i][2 * b + 1], q2_pair(nh, b), acc);
+      }
+      out = fmaf(ds, acc, fmaf(-ms, a.sum[i], out));
+    }
+    return out;
   }
   // codes as bf16 pairs (128 + q_p, 128 + q_{p+8}) against the activation
   // pairs: sum a*(128+q) - 128*sum(a) = sum a*q
@@ -676,6 +742,9 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
             const float v = silu_mul(g[t], u[t]);
             if (am == kAF32) {
               a[(size_t)(rb + t) * I + row] = v;
+            } else if (am == kAF16Q2K) {
+              a_hi[(size_t)(rb + t) * I + q2k16_pos(row)] =
+                  __builtin_bit_cast(uint16_t, (_Float16)v);
             } else {
               uint32_t h, l;
               split_bf16(v, h, l);

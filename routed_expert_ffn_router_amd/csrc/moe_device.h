@@ -41,6 +41,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// acc + a.lo*b.lo + a.hi*b.hi on fp16 pairs (v_dot2_f32_f16)
+typedef _Float16 f16x2_dev_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_dev_t, a),
+                                __builtin_bit_cast(f16x2_dev_t, b), acc, false);
+}
+
 // two E2M1 nibbles (byte `sel` of w, low nibble first) -> bf16 pair, exact
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
