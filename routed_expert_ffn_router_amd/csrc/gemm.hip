@@ -107,6 +107,7 @@ struct GemmArgs {
   int a_rows;                // rows of x (gate/up: T) or of a16 (down: n_rows)
   const int32_t *tiles;
   int weight_major;          // tile order: weights-first (one dense expert) or rows-first
+  int a_swap;                // gate/up: a_out in Q2K slot order (swap12 within each 4 columns)
   uint16_t *a_out;           // gate/up: fp16 [n_rows][N]
   float *y_out;              // down: fp32 [n_rows][N]
 };
@@ -116,6 +117,8 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) { return pack_h2(bf16_lo(v), bf16_hi(v)); }
+// the slot of value i when each group of 4 is ordered (0, 2, 1, 3)
+__device__ __forceinline__ int swap12(int i) { return (i & ~3) | ((i & 1) << 1) | ((i >> 1) & 1); }
 
 // ---------------------------------------------------------------------------
 // B: the weights of one row that a lane covers, raw bits -> operand pairs.
@@ -165,7 +168,7 @@ struct BGroup {
   }
 
   // stage S of the group: the run's weights 16 S .. 16 S + 15; out[i] holds
-  // weights (2i, 2i + 1) of those as an OP pair
+  // weights (2i, 2i + 1) of those as an OP pair (Q2K: in swap12 order)
   __device__ __forceinline__ void decode(int S, uint32_t (&out)[8], const uint2 *cb) const {
     if constexpr (FMT == MOE_FMT_VQ2) {
       // fp16 codebook integers (exact) times the fp16 scale, rounded once
@@ -178,27 +181,24 @@ struct BGroup {
         out[2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * d2);
       }
     } else if constexpr (FMT == MOE_FMT_Q2K) {
-      // the sub-block's four possible weights (q = 0..3), exact in fp32 up to
-      // the final subtraction, rounded to fp16: a byte lookup table
+      // w = (d sc) q - dmin m: the codes widened to E2M1 nibbles (q reads as
+      // q/2) and converted with the scale 2 give q exactly as fp16 pairs;
+      // one fused multiply-add with d sc and -dmin m (each rounded to fp16)
+      // rounds the weight once.  Nibble order pairs weights (4b, 4b+2) and
+      // (4b+1, 4b+3): the A operand is stored in that order (swap12).
       const uint32_t scm = (s0 >> (8 * S)) & 255u;
       const float d = f16_bits_to_f32(s1 & 0xFFFFu), dmin = f16_bits_to_f32(s1 >> 16);
       const float ds = d * (float)(scm & 15u), ms = dmin * (float)(scm >> 4);
-      const uint32_t lut_lo = pack_h2(-ms, ds - ms);
-      const uint32_t lut_hi = pack_h2(2.0f * ds - ms, 3.0f * ds - ms);
-      // selector bytes 2q, 2q + 1 of each weight pair: weight 4b + t sits in
-      // bits 8b + 2t of the dword
+      const f16x2_t ds2 = {(_Float16)ds, (_Float16)ds};
+      const f16x2_t nms2 = {(_Float16)(-ms), (_Float16)(-ms)};
       const uint32_t x = q[S];
-      const uint32_t el = (x << 1) & 0x06060606u;  // byte b: 2 q(4b)
-      const uint32_t ol = (x >> 1) & 0x06060606u;  // byte b: 2 q(4b+1)
-      const uint32_t eh = (x >> 3) & 0x06060606u;  // byte b: 2 q(4b+2)
-      const uint32_t oh = (x >> 5) & 0x06060606u;  // byte b: 2 q(4b+3)
+      const uint32_t nl = x & 0x33333333u, nh = (x >> 2) & 0x33333333u;
 #pragma unroll
       for (int b = 0; b < 4; b++) {
-        const uint32_t sel_b = (uint32_t)b * 0x01010101u + 0x04040000u;  // bytes b, b, 4+b, 4+b
-        const uint32_t s_lo = __builtin_amdgcn_perm(ol, el, sel_b) | 0x01000100u;
-        const uint32_t s_hi = __builtin_amdgcn_perm(oh, eh, sel_b) | 0x01000100u;
-        out[2 * b] = __builtin_amdgcn_perm(lut_hi, lut_lo, s_lo);
-        out[2 * b + 1] = __builtin_amdgcn_perm(lut_hi, lut_lo, s_hi);
+        const f16x2_t p0 = __builtin_bit_cast(f16x2_t, q2_pair(nl, b));
+        const f16x2_t p1 = __builtin_bit_cast(f16x2_t, q2_pair(nh, b));
+        out[2 * b] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(p0, ds2, nms2));
+        out[2 * b + 1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(p1, ds2, nms2));
       }
     } else {  // MXFP4: E2M1 x 2^(e - 127), converted with the scale applied
       const float sc = e8m0_to_f32((s0 >> (8 * (S / 2))) & 255u);
@@ -470,7 +470,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 #pragma unroll
         for (int c = 0; c < NB / 2; c++) {
           const float a = silu_mul(acc[m][c][i], acc[m][c + NB / 2][i]);
-          p.a_out[(size_t)r * p.N + n0 + kWaveCols * wave + 16 * c + lr] =
+          const int col = n0 + kWaveCols * wave + 16 * c + lr;
+          p.a_out[(size_t)r * p.N + (p.a_swap ? swap12(col) : col)] =
               __builtin_bit_cast(uint16_t, (_Float16)a);
         }
       } else {
@@ -598,14 +599,20 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_skinny(SkinnyArgs p) {
 
 // bf16 tokens -> fp16 operands (round to nearest even; exact for every bf16
 // value inside the fp16 normal range), once per call instead of once per
-// column block of the gate/up GEMM
+// column block of the gate/up GEMM.  SWAP: each group of 4 in swap12 order
+// (the Q2K weights' slot order)
+template <bool SWAP>
 __global__ __launch_bounds__(256) void k_tokens_f16(long n8, const uint4 *__restrict__ x,
                                                      uint4 *__restrict__ x16) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const uint4 v = x[i];
-  x16[i] = make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
-                      bf16x2_to_f16x2(v.w));
+  if constexpr (SWAP)
+    x16[i] = make_uint4(pack_h2(bf16_lo(v.x), bf16_lo(v.y)), pack_h2(bf16_hi(v.x), bf16_hi(v.y)),
+                        pack_h2(bf16_lo(v.z), bf16_lo(v.w)), pack_h2(bf16_hi(v.z), bf16_hi(v.w)));
+  else
+    x16[i] = make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+                        bf16x2_to_f16x2(v.w));
 }
 
 // K a multiple of 256 (whole Q2K / VQ2 groups; a whole number of register
@@ -659,7 +666,8 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   if (gateup_op(gate.fmt) == kOpF16) {
     if (mark) mark(mark_ctx, names[3]);
     const long n8 = (long)T * H / 8;  // H % 256 == 0
-    err = launch(k_tokens_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, n8,
+    const auto kern = gate.fmt == MOE_FMT_Q2K ? k_tokens_f16<true> : k_tokens_f16<false>;
+    err = launch(kern, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, n8,
                  reinterpret_cast<const uint4 *>(x), reinterpret_cast<uint4 *>(x16));
     if (err != hipSuccess) return err;
     x = x16;
@@ -669,6 +677,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.x = x, g.a_rows = T;
   g.row_token = offsets ? sorted_token : nullptr;
   g.tiles = tiles, g.a_out = a16;
+  g.a_swap = down.fmt == MOE_FMT_Q2K;
   // one dense expert with many row tiles: keep each weight block in an L2
   g.weight_major = !offsets && (I / block_cols<kModeGateUp, MOE_FMT_BF16>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);

@@ -382,6 +382,17 @@ def test_expert_ffn_gemm_q2(dev, q2, dq2, T):
     assert _gemm_rows_case(q2, dq2, dev, x, off, st, 48, T) < TOL
 
 
+@pytest.mark.parametrize("T", [40, 300, 1100])
+def test_expert_ffn_gemm_q2k_gateup(dev, T):
+    """Q2K gate, up and down on the GEMM path (16-, 64- and 128-row tiles)."""
+    spec = synth.LayerSpec("q2k_gemm", 512, 256, 8, 2, synth.FMT_Q2K, synth.FMT_Q2K,
+                           synth.FMT_Q2K, 256)
+    layer = synth.gen_layer(spec, seed=7)
+    dl = moe.DeviceLayer.upload(layer, device=dev)
+    y, ref = _bucketed_ffn_case(layer, dl, dev, T, 100 + T)
+    assert normwise(y, ref) < TOL
+
+
 def test_expert_ffn_gemm_mxfp4(dev, mx, dmx):
     T = 150
     x = synth.gen_x(4096, T, seed=80)
