@@ -319,6 +319,56 @@ def test_forward_decode_b1_selection_edges(dev, q2, dq2):
         assert bits_equal(tnp(w).reshape(1, 8), tnp(w2)), n
 
 
+def _graph_replays(f, xs, tids=None):
+    """Capture one forward in a HIP graph, replay it once per input with
+    eager work and synchronisations between the replays; every replay must
+    equal the eager run of the same input bit for bit."""
+    refs = []
+    for i, x in enumerate(xs):
+        f(x, None, None if tids is None else tids[i])
+        torch.cuda.synchronize()
+        refs.append((f.out.clone(), f.idx.clone(), f.w.clone()))
+    xb = xs[0].clone()
+    tb = None if tids is None else tids[0].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        f(xb, None, tb)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f(xb, None, tb)
+    for rep in range(2):
+        for i, x in enumerate(xs):
+            xb.copy_(x)
+            if tb is not None:
+                tb.copy_(tids[i])
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(f.out, refs[i][0]), (rep, i)
+            assert torch.equal(f.idx, refs[i][1]) and torch.equal(f.w, refs[i][2]), (rep, i)
+            f(xs[(i + 1) % len(xs)], None, None if tids is None else tids[(i + 1) % len(xs)])
+            torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 16, 300])
+def test_forward_graph_replay(dev, q2, dq2, T):
+    f = moe.Forward(dq2, T, dev)
+    xs = [t16(synth.gen_x(4096, T, seed=300 + 7 * T + i), dev) for i in range(3)]
+    _graph_replays(f, xs)
+
+
+def test_forward_graph_replay_mxfp4_hash_a8(dev, mx, dmx):
+    """Hash routing with MX-FP8 activations (quantization pass + FP4 MFMA)."""
+    layer = dmx.with_route_mode(moe.ROUTE_HASH).with_act(moe.ACT_MXFP8)
+    T = 40
+    f = moe.Forward(layer, T, dev)
+    xs = [t16(synth.gen_x(4096, T, seed=400 + i), dev) for i in range(3)]
+    tids = [torch.from_numpy(synth.gen_token_ids(T, 0, i)).to(dev) for i in range(3)]
+    _graph_replays(f, xs, tids)
+
+
 def test_forward_deterministic(dev, q2, dq2):
     x = t16(synth.gen_x(4096, 16, seed=5), dev)
     a, _, _ = moe.forward(dq2, x)
