@@ -82,6 +82,7 @@ WORKLOADS = {
         Workload("decode_b1", Q2, 1),
         Workload("decode_b16_zipf", Q2, 16, logits="zipf"),
         Workload("prefill_2048", Q2, 2048),
+        Workload("prefill_4096", Q2, 4096),
         Workload("mxfp4_decode_b1", MX, 1),
         Workload("mxfp4_hash_decode_b1", MX, 1, route=ROUTE_HASH),
         Workload("mxfp4_prefill_4096", MX, 4096),

@@ -434,7 +434,8 @@ def test_expert_ffn_gemm_q2(dev, q2, dq2, T):
 
 @pytest.mark.parametrize("T", [40, 300, 1100])
 def test_expert_ffn_gemm_q2k_gateup(dev, T):
-    """Q2K gate, up and down on the GEMM path (16-, 64- and 128-row tiles)."""
+    """Q2K gate, up and down on the GEMM path (16- and 64-row tiles, up to
+    four tiles per expert)."""
     spec = synth.LayerSpec("q2k_gemm", 512, 256, 8, 2, synth.FMT_Q2K, synth.FMT_Q2K,
                            synth.FMT_Q2K, 256)
     layer = synth.gen_layer(spec, seed=7)
@@ -463,7 +464,7 @@ def test_expert_ffn_gemm_ragged_buckets(dev, q2, dq2):
 
 
 def test_expert_ffn_gemm_ragged_buckets_128(dev, q2, dq2):
-    """Bucket sizes around the 128-row tile (enough rows for 128-row tiles)."""
+    """Bucket sizes around 128 rows (up to three 64-row tiles per expert)."""
     sizes = np.array([0, 1, 127, 128, 129, 255, 256, 257, 95, 96, 97, 300] * 22)[:256]
     assert sizes.sum() >= 96 * 256
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
