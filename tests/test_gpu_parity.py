@@ -264,6 +264,32 @@ def test_forward_decode_b1(dev, q2, dq2):
         _forward_case(q2, dq2, dev, 1, seed)
 
 
+# one-token layers of other shapes: H 2048, I 4096, no shared expert, a wide
+# shared expert whose rows take several rounds of p2's waves, MXFP4 with hash
+# routing, few experts and odd k
+_DECODE_SHAPES = [
+    ("h2048_k1_shared4096", 2048, 2048, 8, 1, "vq2", "vq2", "q2k", 4096),
+    ("h2048_i4096_noshared", 2048, 4096, 16, 4, "vq2", "vq2", "q2k", 0),
+    ("h2048_e16_k6", 2048, 2048, 16, 6, "vq2", "vq2", "q2k", 2048),
+    ("h2048_mxfp4", 2048, 2048, 12, 3, "mxfp4", "mxfp4", "mxfp4", 2048),
+    ("h4096_bf16_down", 4096, 2048, 8, 2, "vq2", "vq2", "bf16", 2048),
+]
+_FMT = {"bf16": synth.FMT_BF16, "q2k": synth.FMT_Q2K, "vq2": synth.FMT_VQ2,
+        "mxfp4": synth.FMT_MXFP4}
+
+
+@pytest.mark.parametrize("shape", _DECODE_SHAPES, ids=[c[0] for c in _DECODE_SHAPES])
+def test_forward_decode_shapes(dev, shape):
+    name, H, I, E, k, fg, fu, fd, Is = shape
+    spec = synth.LayerSpec(name, H, I, E, k, _FMT[fg], _FMT[fu], _FMT[fd], Is)
+    layer = synth.gen_layer(spec, seed=11)
+    dl = moe.DeviceLayer.upload(layer, device=dev)
+    for seed in range(2):
+        _forward_case(layer, dl, dev, 1, 500 + seed)
+    if fg == "mxfp4":
+        _forward_case(layer, dl, dev, 1, 510, route=moe.ROUTE_HASH)
+
+
 def test_forward_decode_b16_zipf(dev, q2, dq2):
     _forward_case(q2, dq2, dev, 16, 0, zipf=True)
 
