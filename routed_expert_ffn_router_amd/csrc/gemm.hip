@@ -5,8 +5,8 @@
 // hysenlabs.com "SSD streaming"; matrix-instruction expert kernels on newer
 // devices -- hysenlabs.com "Model support and quantization").  Each workgroup
 // computes BM bucket rows of one expert against 256 weight rows (gate/up: 128
-// gate + 128 up; down: 256 outputs), BM in {16, 64, 128} by the rows per
-// active expert.  Each of the 4 waves owns 64 weight rows for all BM rows and
+// gate + 128 up; down: 256 outputs), BM 16 or 64 by the rows per active
+// expert, 128 for one dense expert.  Each of the 4 waves owns 64 weight rows for all BM rows and
 // dequantizes them straight into MFMA operand registers -- every weight is
 // decoded once per tile and never passes through LDS; only the activation
 // rows (gathered tokens, or the SwiGLU output in bucket order) are staged in
