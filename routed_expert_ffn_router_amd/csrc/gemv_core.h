@@ -171,28 +171,6 @@ struct ADown<MOE_FMT_Q2K, SPL, LPR> {
       sum[i] = s;
     }
   }
-  // activations already split by the producer into bf16 hi/lo arrays, each
-  // 16-value piece stored in pair order (a[p], a[p+8]) at dword p
-  __device__ __forceinline__ void load_split(const uint16_t *hi_row, const uint16_t *lo_row,
-                                             int kl) {
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(hi_row, 0x7FFFFFFF);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lo_row, 0x7FFFFFFF);
-#pragma unroll
-    for (int i = 0; i < SPL; i++) {
-      const uint32_t vo = 2u * (uint32_t)piece_k<LPR>(kl, i);
-      const u32x4_t h0 = buf_u128(rh, vo, 0), h1 = buf_u128(rh, vo + 16, 0);
-      const u32x4_t l0 = buf_u128(rl, vo, 0), l1 = buf_u128(rl, vo + 16, 0);
-      hi[i][0] = h0.x, hi[i][1] = h0.y, hi[i][2] = h0.z, hi[i][3] = h0.w;
-      hi[i][4] = h1.x, hi[i][5] = h1.y, hi[i][6] = h1.z, hi[i][7] = h1.w;
-      lo[i][0] = l0.x, lo[i][1] = l0.y, lo[i][2] = l0.z, lo[i][3] = l0.w;
-      lo[i][4] = l1.x, lo[i][5] = l1.y, lo[i][6] = l1.z, lo[i][7] = l1.w;
-      float s = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 8; m++)
-        s += (bf16_lo(hi[i][m]) + bf16_lo(lo[i][m])) + (bf16_hi(hi[i][m]) + bf16_hi(lo[i][m]));
-      sum[i] = s;
-    }
-  }
 };
 
 // BF16 weights: bf16 hi/lo pairs (a[2m], a[2m+1]) matching the weight dwords
@@ -234,13 +212,9 @@ struct ADown<MOE_FMT_BF16, SPL, LPR> {
 
 // How a gate/up kernel stores the SwiGLU output a for the down kernel:
 // kAF32: fp32; kASplit: bf16 hi/lo arrays in natural order (bf16 down);
-// kASplitQ2K: bf16 hi/lo with each 16-value piece in Q2K pair order;
 // kAF16Q2K: fp16 (one array), each 16-value piece in the order of
 // ADownQ2K16's pairs.
-constexpr int kAF32 = 0, kASplit = 1, kASplitQ2K = 2, kAF16Q2K = 3;
-__device__ __forceinline__ int q2k_pair_pos(int i) {
-  return (i & ~15) | ((i & 7) << 1) | ((i >> 3) & 1);
-}
+constexpr int kAF32 = 0, kASplit = 1, kAF16Q2K = 3;
 // value 4b + r of a piece sits at 4b + 2(r & 1) + (r >> 1): the pairs are
 // (a[4b], a[4b+2]) and (a[4b+1], a[4b+3])
 __device__ __forceinline__ int q2k16_pos(int i) {
@@ -748,7 +722,7 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
             } else {
               uint32_t h, l;
               split_bf16(v, h, l);
-              const size_t pos = (size_t)(rb + t) * I + (am == kASplitQ2K ? q2k_pair_pos(row) : row);
+              const size_t pos = (size_t)(rb + t) * I + row;
               a_hi[pos] = (uint16_t)h;
               a_lo[pos] = (uint16_t)l;
             }
