@@ -203,12 +203,14 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
     // formats they are requested first and travel alongside the expert index;
     // MXFP4's wider rows go first instead
     constexpr bool kAFirst = DFMT != MOE_FMT_MXFP4;
-    // Q2K: p2 leaves a as fp16 (kAF16Q2K)
-    using AV = std::conditional_t<DFMT == MOE_FMT_Q2K, ADownQ2K16<DSPL, 64>, ADown<DFMT, DSPL, 64>>;
+    // Q2K and MXFP4: p2 leaves a as fp16 (kAF16Q2K, kAF16)
+    using AV = std::conditional_t<
+        DFMT == MOE_FMT_Q2K, ADownQ2K16<DSPL, 64>,
+        std::conditional_t<DFMT == MOE_FMT_MXFP4, ADownF16<DSPL, 64>, ADown<DFMT, DSPL, 64>>>;
     for (int j = wave; j < p.k; j += kDecWaves) {
       AV av[1];
       auto load_a = [&]() {
-        if constexpr (DFMT == MOE_FMT_Q2K)
+        if constexpr (DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_MXFP4)
           av[0].load(p.a_hi + (size_t)j * p.I, lane);
         else if constexpr (DFMT == MOE_FMT_BF16)
           av[0].load_split(p.a_hi + (size_t)j * p.I, p.a_lo + (size_t)j * p.I, lane);
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
 #pragma unroll
       for (int r = 0; r < kP3Rows; r++) {
         float y[1];
-        if constexpr (DFMT == MOE_FMT_Q2K)
+        if constexpr (DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_MXFP4)
           y[0] = c[r % PF].dot_a16(av[0]);
         else
           c[r % PF].template dot_a<1>(av, cb, y);
@@ -320,7 +322,10 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
   const int rpb = rows_per_block(a.gate.fmt, hs);
   a.tiles_per_expert = (a.I + rpb - 1) / rpb;
   a.nb_routed = a.k * a.tiles_per_expert;
-  a.a_mode = a.down.fmt == MOE_FMT_Q2K ? kAF16Q2K : a.down.fmt == MOE_FMT_BF16 ? kASplit : kAF32;
+  a.a_mode = a.down.fmt == MOE_FMT_Q2K     ? kAF16Q2K
+             : a.down.fmt == MOE_FMT_MXFP4 ? kAF16
+             : a.down.fmt == MOE_FMT_BF16  ? kASplit
+                                           : kAF32;
   hipError_t e;
   if (a.nb_router + a.nb_shared_gu > 0) {
     mark(mark_ctx, "decode_p1");

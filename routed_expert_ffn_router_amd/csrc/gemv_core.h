@@ -213,13 +213,29 @@ struct ADown<MOE_FMT_BF16, SPL, LPR> {
 // How a gate/up kernel stores the SwiGLU output a for the down kernel:
 // kAF32: fp32; kASplit: bf16 hi/lo arrays in natural order (bf16 down);
 // kAF16Q2K: fp16 (one array), each 16-value piece in the order of
-// ADownQ2K16's pairs.
-constexpr int kAF32 = 0, kASplit = 1, kAF16Q2K = 3;
+// ADownQ2K16's pairs; kAF16: fp16 in natural order (MXFP4 down).
+constexpr int kAF32 = 0, kASplit = 1, kAF16Q2K = 3, kAF16 = 4;
 // value 4b + r of a piece sits at 4b + 2(r & 1) + (r >> 1): the pairs are
 // (a[4b], a[4b+2]) and (a[4b+1], a[4b+3])
 __device__ __forceinline__ int q2k16_pos(int i) {
   return (i & ~3) | ((i & 1) << 1) | ((i >> 1) & 1);
 }
+
+// fp16 activations in natural order: per piece the pairs (a[2m], a[2m+1])
+template <int SPL, int LPR>
+struct ADownF16 {
+  uint32_t h[SPL][8];
+  __device__ __forceinline__ void load(const uint16_t *row, int kl) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(row, 0x7FFFFFFF);
+#pragma unroll
+    for (int i = 0; i < SPL; i++) {
+      const uint32_t vo = 2u * (uint32_t)piece_k<LPR>(kl, i);
+      const u32x4_t a0 = buf_u128(r, vo, 0), a1 = buf_u128(r, vo + 16, 0);
+      h[i][0] = a0.x, h[i][1] = a0.y, h[i][2] = a0.z, h[i][3] = a0.w;
+      h[i][4] = a1.x, h[i][5] = a1.y, h[i][6] = a1.z, h[i][7] = a1.w;
+    }
+  }
+};
 
 // the two 2-bit codes held as E2M1 nibbles in byte b of w, as an exact fp16
 // pair (E2M1 codes 0..3 are 0, 0.5, 1, 1.5; the scale 2 makes them 0..3)
@@ -515,6 +531,24 @@ struct Chunk<MOE_FMT_MXFP4, SPL, LPR> {
       for (int t = 0; t < NT; t++) out[t] = fmaf(acc[t], s, out[t]);
     }
   }
+  // against fp16 activations: the E2M1 pairs converted exactly to fp16 (scale
+  // 1), one v_dot2_f32_f16 per pair, the block scale once per 32 weights
+  __device__ __forceinline__ float dot_a16(const ADownF16<SPL, LPR> &a) const {
+    float out = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPL; i++) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        acc = dot2_f16(a.h[i][4 * j + 0], e2m1x2_to_f16x2<0>(v[i][j]), acc);
+        acc = dot2_f16(a.h[i][4 * j + 1], e2m1x2_to_f16x2<1>(v[i][j]), acc);
+        acc = dot2_f16(a.h[i][4 * j + 2], e2m1x2_to_f16x2<2>(v[i][j]), acc);
+        acc = dot2_f16(a.h[i][4 * j + 3], e2m1x2_to_f16x2<3>(v[i][j]), acc);
+      }
+      out = fmaf(acc, e8m0_to_f32(sc[i]), out);
+    }
+    return out;
+  }
   template <int NT>
   __device__ __forceinline__ void dot_a(const ADown<MOE_FMT_MXFP4, SPL, LPR> (&a)[NT],
                                         const uint2 *, float (&out)[NT]) const {
@@ -716,8 +750,8 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
             const float v = silu_mul(g[t], u[t]);
             if (am == kAF32) {
               a[(size_t)(rb + t) * I + row] = v;
-            } else if (am == kAF16Q2K) {
-              a_hi[(size_t)(rb + t) * I + q2k16_pos(row)] =
+            } else if (am == kAF16Q2K || am == kAF16) {
+              a_hi[(size_t)(rb + t) * I + (am == kAF16Q2K ? q2k16_pos(row) : row)] =
                   __builtin_bit_cast(uint16_t, (_Float16)v);
             } else {
               uint32_t h, l;

@@ -48,6 +48,12 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
                                 __builtin_bit_cast(f16x2_dev_t, b), acc, false);
 }
 
+// two E2M1 nibbles (byte `sel` of w, low nibble first) -> fp16 pair, exact
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
 // two E2M1 nibbles (byte `sel` of w, low nibble first) -> bf16 pair, exact
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
