@@ -122,7 +122,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   asm volatile("" ::"v"(cbw), "v"(lg.v[0]), "v"(lg.v[1]), "v"(lg.v[2]), "v"(lg.v[3]),
                "v"((uint32_t)tid0), "v"((uint32_t)(tid0 >> 32)));
-  if constexpr (RFMT == MOE_FMT_VQ2) codebook_entry_store<kDecThreads>(cbw, s_cb);
+  // the codebook copies are written by waves 4-7 alone, so that wave 0
+  // goes straight to the selection
+  if constexpr (RFMT == MOE_FMT_VQ2)
+    if (wave >= 4) codebook_entry_store_all(cbw, s_cb);
   if (wave == 0) {
     // the selection is the block's critical path: its wave issues first
     __builtin_amdgcn_s_setprio(3);

@@ -650,6 +650,16 @@ __device__ __forceinline__ void fill_codebook(const int8_t *cb, uint2 *s_cb) {
 __device__ __forceinline__ uint32_t codebook_entry_load(const int8_t *cb) {
   return reinterpret_cast<const uint32_t *>(cb)[threadIdx.x & 255];
 }
+// entry threadIdx.x % 256, every copy (for 256 of the block's threads)
+__device__ __forceinline__ void codebook_entry_store_all(uint32_t w, uint2 *s_cb) {
+  uint32_t b[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) b[j] = f32_to_bf16_bits((float)(int)(int8_t)((w >> (8 * j)) & 255u));
+  const uint2 v = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  const int e = threadIdx.x & 255;
+#pragma unroll
+  for (int c = 0; c < kNCopy; c++) s_cb[e * kNCopy + c] = v;
+}
 template <int N>
 __device__ __forceinline__ void codebook_entry_store(uint32_t w, uint2 *s_cb) {
   static_assert(N % 256 == 0, "thread count");
