@@ -327,7 +327,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       h[j] = pack_h2((float)(int)(int8_t)((cw >> (16 * j)) & 255u),
                      (float)(int)(int8_t)((cw >> (16 * j + 8)) & 255u));
 #pragma unroll
-    for (int c = 0; c < kNCopy; c++) s_cb[tid * kNCopy + c] = make_uint2(h[0], h[1]);
+    for (int j = 0; j < kNCopy; j++)  // a different copy per lane and step: no bank conflicts
+      s_cb[tid * kNCopy + ((j + tid) & (kNCopy - 1))] = make_uint2(h[0], h[1]);
   }
 
   // A staging: row tid / (256 / BM), LDS columns acol .. acol + BM / 4 - 1

@@ -640,7 +640,7 @@ __device__ __forceinline__ void fill_codebook(const int8_t *cb, uint2 *s_cb) {
     for (int j = 0; j < 4; j++) b[j] = f32_to_bf16_bits((float)(int)(int8_t)((w >> (8 * j)) & 255u));
     const uint2 v = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 #pragma unroll
-    for (int c = 0; c < kNCopy; c++) s_cb[e * kNCopy + c] = v;
+    for (int j = 0; j < kNCopy; j++) s_cb[e * kNCopy + ((j + e) & (kNCopy - 1))] = v;
   }
 }
 
@@ -657,8 +657,10 @@ __device__ __forceinline__ void codebook_entry_store_all(uint32_t w, uint2 *s_cb
   for (int j = 0; j < 4; j++) b[j] = f32_to_bf16_bits((float)(int)(int8_t)((w >> (8 * j)) & 255u));
   const uint2 v = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   const int e = threadIdx.x & 255;
+  // lanes write different copies in each step (consecutive entries are 128
+  // bytes apart: the same copy for all lanes would hit one bank pair)
 #pragma unroll
-  for (int c = 0; c < kNCopy; c++) s_cb[e * kNCopy + c] = v;
+  for (int j = 0; j < kNCopy; j++) s_cb[e * kNCopy + ((j + threadIdx.x) & (kNCopy - 1))] = v;
 }
 template <int N>
 __device__ __forceinline__ void codebook_entry_store(uint32_t w, uint2 *s_cb) {
@@ -669,7 +671,8 @@ __device__ __forceinline__ void codebook_entry_store(uint32_t w, uint2 *s_cb) {
   const uint2 v = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   const int e = threadIdx.x & 255;
 #pragma unroll
-  for (int c = threadIdx.x >> 8; c < kNCopy; c += N / 256) s_cb[e * kNCopy + c] = v;
+  for (int c = threadIdx.x >> 8; c < kNCopy; c += N / 256)
+    s_cb[e * kNCopy + ((c + e) & (kNCopy - 1))] = v;
 }
 
 // rows per wave step so the raw bits in flight stay near 32 dwords per lane
