@@ -40,6 +40,28 @@ __device__ __forceinline__ float wave_max_f(float v) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+// the same maximum / minimum in every lane, with VALU operations only: DPP
+// within rows of 16, then the row-pair and half-wave swaps of gfx950
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ int wave_min_all(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = min((int)r[0], (int)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return min((int)q[0], (int)q[1]);
+}
 __device__ __forceinline__ int wave_min_i(int v) {
   v = min(v, dpp_i<0xB1>(v));
   v = min(v, dpp_i<0x4E>(v));

@@ -95,13 +95,10 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
     order(1, 3);
     order(1, 2);
     for (int j = 0; j < k; j++) {
-      const float m = wave_max_f(v[0]);
-      const uint64_t tied = __ballot(v[0] == m);
-      int e;
-      if ((tied & (tied - 1)) == 0)
-        e = __builtin_amdgcn_readlane(id[0], __builtin_ctzll(tied));
-      else  // several heads equal: the lowest index among them
-        e = wave_min_i(v[0] == m ? id[0] : 0x7FFFFFFF);
+      // the largest head, then the lowest index among heads equal to it,
+      // both reduced in VALU registers (no round trips through scalars)
+      const float m = wave_max_all(v[0]);
+      const int e = wave_min_all(v[0] == m ? id[0] : 0x7FFFFFFF);
       const bool pop = lane == (e & 63);
       v[0] = pop ? v[1] : v[0];
       id[0] = pop ? id[1] : id[0];
