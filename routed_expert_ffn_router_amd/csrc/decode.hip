@@ -241,11 +241,8 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
         acc[r] = fmaf(wj, y[0], acc[r]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < kP3Rows; r++) {
-      const float v = wave_sum_f(acc[r]);
-      if (lane == 0) s_part[wave][r] = v;
-    }
+    const float v = rows_reduce<kP3Rows>(acc);
+    if ((lane & (64 / kP3Rows - 1)) == 0) s_part[wave][lane / (64 / kP3Rows)] = v;
   }
   __syncthreads();
   if ((int)threadIdx.x < kP3Rows) {

@@ -82,6 +82,52 @@ __device__ __forceinline__ float wave_sum_f(float v) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }
 
+// R per-row partial sums (R = 8 or 16) in every lane -> the R row totals,
+// transposed: each step pairs lanes across one lane bit (the half-wave swap,
+// the row-pair swap, then DPP inside rows of 16) and keeps half of the rows,
+// so the R totals cost about 2R instructions instead of R full reductions.
+// Lane l returns the total of row l / (64 / R).
+template <int R>
+__device__ __forceinline__ float rows_reduce(const float (&v)[R]) {
+  static_assert(R == 8 || R == 16, "rows");
+  const int lane = threadIdx.x & 63;
+  float w[R / 2];
+#pragma unroll
+  for (int r = 0; r < R / 2; r++) {
+    // lanes < 32 keep row r (both halves' sum), lanes >= 32 row r + R/2
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[r]),
+                                                    __float_as_uint(v[r + R / 2]), false, false);
+    w[r] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  float u[R / 4];
+#pragma unroll
+  for (int r = 0; r < R / 4; r++) {
+    // even rows of 16 lanes keep w[r], odd ones w[r + R/4]
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[r]),
+                                                    __float_as_uint(w[r + R / 4]), false, false);
+    u[r] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  // lanes l and l ^ 8 (a rotation by 8 inside the row of 16)
+  const bool b3 = lane & 8;
+  float t[R / 8];
+#pragma unroll
+  for (int r = 0; r < R / 8; r++) {
+    const float keep = b3 ? u[r + R / 8] : u[r], send = b3 ? u[r] : u[r + R / 8];
+    t[r] = keep + dpp_f<0x128>(send);
+  }
+  float x;
+  if constexpr (R == 16) {
+    // lanes i and 7 - i of each half-row (the half-row mirror)
+    const bool b2 = lane & 4;
+    const float keep = b2 ? t[1] : t[0], send = b2 ? t[0] : t[1];
+    x = keep + dpp_f<0x141>(send);
+  } else {
+    x = t[0] + dpp_f<0x141>(t[0]);
+  }
+  x += dpp_f<0xB1>(x);
+  return x + dpp_f<0x4E>(x);
+}
+
 // sum over aligned groups of G lanes; G = 64 returns the full sum in all lanes
 template <int G>
 __device__ __forceinline__ float lane_group_sum(float v) {
@@ -460,8 +506,12 @@ struct Chunk<MOE_FMT_Q2K, SPL, LPR> {
     float out = 0.0f;
 #pragma unroll
     for (int i = 0; i < SPL; i++) {
-      const float d = f16_bits_to_f32(dm[i] & 0xFFFFu), dmin = f16_bits_to_f32(dm[i] >> 16);
-      const float ds = d * (float)(sc[i] & 15u), ms = dmin * (float)(sc[i] >> 4);
+      // (d sc, dmin m) as one fp16 pair: the two nibbles as 1024 + n (exact
+      // in fp16), minus 1024, times (d, dmin), rounded once each to fp16
+      const uint32_t nib = (((sc[i] << 12) | sc[i]) & 0x000F000Fu) | 0x64006400u;
+      const f16x2_dev_t sm = (__builtin_bit_cast(f16x2_dev_t, nib) - (_Float16)1024.0f) *
+                             __builtin_bit_cast(f16x2_dev_t, dm[i]);
+      const float ds = (float)sm[0], ms = (float)sm[1];
       const uint32_t nl = qs[i] & 0x33333333u, nh = (qs[i] >> 2) & 0x33333333u;
       float acc = 0.0f;
 #pragma unroll
