@@ -811,6 +811,25 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
           tok_fixed >= 0 ? tok_fixed : (row_token ? row_token[r] : r));
       load_x_pieces<SPL, LPR>(x, H, tok, kl, xw[t]);
     }
+    auto store = [&](int r, int row, float v) {
+      if (am == kAF32) {
+        a[(size_t)r * I + row] = v;
+      } else if (am == kAF16Q2K || am == kAF16) {
+        a_hi[(size_t)r * I + (am == kAF16Q2K ? q2k16_pos(row) : row)] =
+            __builtin_bit_cast(uint16_t, (_Float16)v);
+      } else {
+        uint32_t h, l;
+        split_bf16(v, h, l);
+        const size_t pos = (size_t)r * I + row;
+        a_hi[pos] = (uint16_t)h;
+        a_lo[pos] = (uint16_t)l;
+      }
+    };
+    // one token and four row pairs per wave, all loaded at once: the eight
+    // sums are reduced together at the end (rows_reduce) instead of one full
+    // reduction each
+    constexpr bool kT = LPR == 64 && NT == 1 && STEPS == 4 && D == STEPS;
+    float gs[kT ? STEPS : 1], us[kT ? STEPS : 1];
 #pragma unroll
     for (int s = 0; s < STEPS; s++) {
       const int row = row_base + s * RPS;
@@ -823,30 +842,32 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
         cu[s % D].load(up, e, nrow, kl);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the pipeline depth: no hoisting of later loads
+      if constexpr (kT) {
+        gs[s] = g[0];
+        us[s] = u[0];
+      } else {
 #pragma unroll
-      for (int t = 0; t < NT; t++) {
-        g[t] = lane_group_sum<LPR>(g[t]);
-        u[t] = lane_group_sum<LPR>(u[t]);
-      }
-      if (kl == 0 && row < I) {
+        for (int t = 0; t < NT; t++) {
+          g[t] = lane_group_sum<LPR>(g[t]);
+          u[t] = lane_group_sum<LPR>(u[t]);
+        }
+        if (kl == 0 && row < I) {
 #pragma unroll
-        for (int t = 0; t < NT; t++)
-          if (t < nt) {
-            const float v = silu_mul(g[t], u[t]);
-            if (am == kAF32) {
-              a[(size_t)(rb + t) * I + row] = v;
-            } else if (am == kAF16Q2K || am == kAF16) {
-              a_hi[(size_t)(rb + t) * I + (am == kAF16Q2K ? q2k16_pos(row) : row)] =
-                  __builtin_bit_cast(uint16_t, (_Float16)v);
-            } else {
-              uint32_t h, l;
-              split_bf16(v, h, l);
-              const size_t pos = (size_t)(rb + t) * I + row;
-              a_hi[pos] = (uint16_t)h;
-              a_lo[pos] = (uint16_t)l;
-            }
-          }
+          for (int t = 0; t < NT; t++)
+            if (t < nt) store(rb + t, row, silu_mul(g[t], u[t]));
+        }
       }
+    }
+    if constexpr (kT) {
+      const float vals[8] = {gs[0], gs[1], gs[2], gs[3], us[0], us[1], us[2], us[3]};
+      // lane l: the total of value l / 8 (gate of step l / 8 below lane 32,
+      // up above); the half-wave swap brings each up total next to its gate
+      const float x = rows_reduce<8>(vals);
+      const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                      false);
+      const int row = row_base + (lane >> 3) * RPS;
+      if (lane < 32 && (lane & 7) == 0 && row < I)
+        store(rb, row, silu_mul(__uint_as_float(q[0]), __uint_as_float(q[1])));
     }
   }
 }
