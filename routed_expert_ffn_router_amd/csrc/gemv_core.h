@@ -42,15 +42,15 @@ __device__ __forceinline__ float wave_max_f(float v) {
 }
 // the same maximum / minimum in every lane, with VALU operations only: DPP
 // within rows of 16, then the row-pair and half-wave swaps of gfx950
-__device__ __forceinline__ float wave_max_all(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+__device__ __forceinline__ int wave_max_all(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = max((int)r[0], (int)r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return max((int)q[0], (int)q[1]);
 }
 __device__ __forceinline__ int wave_min_all(int v) {
   v = min(v, dpp_i<0xB1>(v));

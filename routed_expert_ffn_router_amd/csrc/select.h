@@ -22,6 +22,13 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 }
 
 __device__ __forceinline__ float order_val(float v) { return v != v ? -INFINITY : v; }
+// a signed integer with the order of the (non-NaN) float, and back; -0 and +0
+// get different keys, so callers pass +0 for both
+__device__ __forceinline__ int float_key(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float key_float(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
 // The logits a wave needs for one token, loaded up front so that the selection
 // costs one memory round trip: candidate e = lane + 64 i sits in v[i].
@@ -72,17 +79,20 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
     // each lane sorts its four candidates once (value descending, index
     // ascending on ties; NaN and absent candidates as -inf, absent ones after
     // every present one by their index); a round then compares only the
-    // lanes' heads and the winner's lane pops its head
-    float v[4];
+    // lanes' heads and the winner's lane pops its head.  Values are compared
+    // as integer keys with the order of the floats (-0 made +0 first, so
+    // that it ties with +0), which the DPP maximum takes without the float
+    // maximum's NaN handling.
+    int v[4];
     int id[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       id[i] = lane + 64 * i;
-      v[i] = id[i] < E ? order_val(lg.v[i]) : -INFINITY;
+      v[i] = float_key(id[i] < E ? order_val(lg.v[i]) + 0.0f : -INFINITY);
     }
     auto order = [&](int a, int b) {  // afterwards a comes before b
       const bool sw = v[b] > v[a] || (v[b] == v[a] && id[b] < id[a]);
-      const float tv = v[a];
+      const int tv = v[a];
       const int ti = id[a];
       v[a] = sw ? v[b] : v[a];
       id[a] = sw ? id[b] : id[a];
@@ -94,10 +104,12 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
     order(0, 2);
     order(1, 3);
     order(1, 2);
+    const int absent = float_key(-INFINITY);
+    int my_key = absent;
     for (int j = 0; j < k; j++) {
       // the largest head, then the lowest index among heads equal to it,
       // both reduced in VALU registers (no round trips through scalars)
-      const float m = wave_max_all(v[0]);
+      const int m = wave_max_all(v[0]);
       const int e = wave_min_all(v[0] == m ? id[0] : 0x7FFFFFFF);
       const bool pop = lane == (e & 63);
       v[0] = pop ? v[1] : v[0];
@@ -106,13 +118,14 @@ __device__ __forceinline__ void select_wave(int mode, int E, int k, const Logits
       id[1] = pop ? id[2] : id[1];
       v[2] = pop ? v[3] : v[2];
       id[2] = pop ? id[3] : id[2];
-      v[3] = pop ? -INFINITY : v[3];
+      v[3] = pop ? absent : v[3];
       id[3] = pop ? 0x7FFFFFFF : id[3];
       if (lane == j) {
         my_e = e;
-        my_l = m;  // already in selection-order form: NaN reads as -inf
+        my_key = m;
       }
     }
+    my_l = key_float(my_key);  // already in selection-order form: NaN reads as -inf
   } else {
     float v[NC];
     uint32_t taken = 0;  // bit i: candidate lane + 64 i is taken or absent
