@@ -96,8 +96,11 @@ template <int RFMT, int RSPL, int SSPL>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_p2(DecodeArgs p) {
   __shared__ uint2 s_cb[RFMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   __shared__ int s_e[16];
+  __shared__ int s_ready;  // waves whose LDS outputs (selection, codebook) are written
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x == 0) s_ready = 0;
+  __syncthreads();  // (nothing is in flight yet)
   const float *lsrc = p.logits_in ? p.logits_in : p.logits;
   const bool small_e = p.E <= 256;
   // unconditional loads (a branch around them would make the compiler wait
@@ -125,7 +128,11 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   // the codebook copies are written by waves 4-7 alone, so that wave 0
   // goes straight to the selection
   if constexpr (RFMT == MOE_FMT_VQ2)
-    if (wave >= 4) codebook_entry_store_all(cbw, s_cb);
+    if (wave >= 4) {
+      codebook_entry_store_all(cbw, s_cb);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) atomicAdd(&s_ready, 1);
+    }
   if (wave == 0) {
     // the selection is the block's critical path: its wave issues first
     __builtin_amdgcn_s_setprio(3);
@@ -143,6 +150,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
         p.topk_w[lane] = w;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) atomicAdd(&s_ready, 1);
   } else if (p.Is) {
     const int step = gridDim.x * kDecWaves;
     for (int base = rb0; base < p.H; base += step) {
@@ -163,7 +172,17 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
       }
     }
   }
-  __syncthreads();
+  // each wave goes on as soon as the selection and the codebook are written,
+  // without waiting for the other waves' shared rows (a bounded wait on an
+  // LDS counter that waves of this block always complete)
+  {
+    const int need = RFMT == MOE_FMT_VQ2 ? 5 : 1;
+    for (int it = 0; it < (1 << 22); it++) {
+      if (__hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= need) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
   constexpr int ST = steps_for<RFMT, RSPL>();
   const int j = blockIdx.x / p.tiles_per_expert, tile = blockIdx.x % p.tiles_per_expert;
   const int row_base = (tile * kDecWaves + wave) * ST;
