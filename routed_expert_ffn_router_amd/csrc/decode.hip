@@ -94,7 +94,11 @@ __global__ __launch_bounds__(kP1Threads) void k_dec_p1(DecodeArgs p) {
 // ---------------------------------------------------------------------------
 template <int RFMT, int RSPL, int SSPL>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_p2(DecodeArgs p) {
-  __shared__ uint2 s_cb[RFMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
+  // the VQ2 codebook in 32 copies (64 KB; two blocks still fit a CU): each
+  // lane of a half-wave reads its own copy (with 16, lanes l and l + 16 share
+  // one and the lookups took bank conflicts)
+  constexpr int kCopies = 32;
+  __shared__ uint2 s_cb[RFMT == MOE_FMT_VQ2 ? 256 * kCopies : 1];
   __shared__ int s_e[16];
   __shared__ int s_ready;  // waves whose LDS outputs (selection, codebook) are written
   const int lane = threadIdx.x & 63;
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   // goes straight to the selection
   if constexpr (RFMT == MOE_FMT_VQ2)
     if (wave >= 4) {
-      codebook_entry_store_all(cbw, s_cb);
+      codebook_entry_store_all<kCopies>(cbw, s_cb);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       if (lane == 0) atomicAdd(&s_ready, 1);
     }
@@ -189,9 +193,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   const int e_sel = __builtin_amdgcn_readfirstlane(s_e[j]);
   // every routed row pair's loads go out at once (MXFP4's larger chunks: two)
   constexpr int kRPF = RFMT == MOE_FMT_MXFP4 ? 2 : ST;
-  gateup_rows<RFMT, RSPL, 64, ST, 1, kRPF>(p.gate, p.up, p.H, p.I, p.x, e_sel, j, j + 1, nullptr, 0,
-                                           p.a, row_base, s_cb + (lane % kNCopy), p.a_mode, p.a_hi,
-                                           p.a_lo);
+  gateup_rows<RFMT, RSPL, 64, ST, 1, kRPF, kCopies>(p.gate, p.up, p.H, p.I, p.x, e_sel, j, j + 1,
+                                                    nullptr, 0, p.a, row_base,
+                                                    s_cb + (lane % kCopies), p.a_mode, p.a_hi,
+                                                    p.a_lo);
 }
 
 // ---------------------------------------------------------------------------

@@ -386,8 +386,8 @@ struct Chunk<MOE_FMT_VQ2, SPL, LPR> {
       d[i] = buf_u16(rs, vs + (k / 256) * 2, ss);
     }
   }
-  // cb: this lane's codebook copy in LDS (entry e at cb[e * kNCopy])
-  template <int NT>
+  // cb: this lane's codebook copy in LDS (entry e at cb[e * NC], NC copies)
+  template <int NT, int NC = kNCopy>
   __device__ __forceinline__ void dot_x(const uint32_t (&xw)[NT][SPL][8], const uint2 *cb,
                                         float (&out)[NT]) const {
 #pragma unroll
@@ -399,7 +399,7 @@ struct Chunk<MOE_FMT_VQ2, SPL, LPR> {
       for (int t = 0; t < NT; t++) acc[t] = 0.0f;
 #pragma unroll
       for (int b = 0; b < 4; b++) {
-        const uint2 c = cb[((code[i] >> (8 * b)) & 255u) * kNCopy];
+        const uint2 c = cb[((code[i] >> (8 * b)) & 255u) * NC];
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           acc[t] = dot2_bf16(xw[t][i][2 * b], c.x, acc[t]);
@@ -722,7 +722,8 @@ __device__ __forceinline__ void fill_codebook(const int8_t *cb, uint2 *s_cb) {
 __device__ __forceinline__ uint32_t codebook_entry_load(const int8_t *cb) {
   return reinterpret_cast<const uint32_t *>(cb)[threadIdx.x & 255];
 }
-// entry threadIdx.x % 256, every copy (for 256 of the block's threads)
+// entry threadIdx.x % 256, every one of NC copies (for 256 of the block's threads)
+template <int NC = kNCopy>
 __device__ __forceinline__ void codebook_entry_store_all(uint32_t w, uint2 *s_cb) {
   uint32_t b[4];
 #pragma unroll
@@ -732,7 +733,7 @@ __device__ __forceinline__ void codebook_entry_store_all(uint32_t w, uint2 *s_cb
   // lanes write different copies in each step (consecutive entries are 128
   // bytes apart: the same copy for all lanes would hit one bank pair)
 #pragma unroll
-  for (int j = 0; j < kNCopy; j++) s_cb[e * kNCopy + ((j + threadIdx.x) & (kNCopy - 1))] = v;
+  for (int j = 0; j < NC; j++) s_cb[e * NC + ((j + threadIdx.x) & (NC - 1))] = v;
 }
 template <int N>
 __device__ __forceinline__ void codebook_entry_store(uint32_t w, uint2 *s_cb) {
@@ -780,7 +781,7 @@ __host__ __device__ inline bool gemv_geometry(int K, int *spl, int *lpr) {
 
 // a[r][row] = silu(gate_e[row] . x_t) * (up_e[row] . x_t) for bucket rows
 // r in [r0, r1), token of row r = row_token[r] (or tok_fixed >= 0, or r)
-template <int FMT, int SPL, int LPR, int STEPS, int NT, int PF = 2>
+template <int FMT, int SPL, int LPR, int STEPS, int NT, int PF = 2, int NC = kNCopy>
 __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, int H, int I,
                                             const uint16_t *x, int e, int r0, int r1,
                                             const int32_t *row_token, int tok_fixed, float *a,
@@ -834,8 +835,13 @@ __device__ __forceinline__ void gateup_rows(const WView &gate, const WView &up, 
     for (int s = 0; s < STEPS; s++) {
       const int row = row_base + s * RPS;
       float g[NT], u[NT];
-      cg[s % D].template dot_x<NT>(xw, cb, g);
-      cu[s % D].template dot_x<NT>(xw, cb, u);
+      if constexpr (FMT == MOE_FMT_VQ2) {
+        cg[s % D].template dot_x<NT, NC>(xw, cb, g);
+        cu[s % D].template dot_x<NT, NC>(xw, cb, u);
+      } else {
+        cg[s % D].template dot_x<NT>(xw, cb, g);
+        cu[s % D].template dot_x<NT>(xw, cb, u);
+      }
       if (s + D < STEPS) {  // refill this slot with the row D steps ahead
         const int nrow = min(row_base + (s + D) * RPS, I - 1);
         cg[s % D].load(gate, e, nrow, kl);
