@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -131,6 +132,39 @@ struct Marker {
 };
 
 void mark_cb(void *ctx, const char *name) { (*static_cast<Marker *>(ctx))(name); }
+
+// A second stream per device (default priority) with a fork and a join
+// event: the shared expert does not depend on the routing, so moe_forward runs
+// it there, beside the router, the selection, the dispatch and the routed
+// FFN, and joins before the combine.  Created once per device on first use;
+// null (everything on the caller's stream) if that fails.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+SideStream *side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream &ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    ss.s = st, ss.fork = f, ss.join = j;
+  }
+  return &ss;
+}
 
 WView bf16_view(const uint16_t *p, int N, int K) {
   return WView{MOE_FMT_BF16, 1, N, K, reinterpret_cast<const uint8_t *>(p), nullptr, nullptr};
@@ -486,76 +520,98 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     a.topk_idx = idx, a.topk_w = w, a.out = out_f32, a.out_bf16 = out_bf16;
     return hip_check(launch_decode1(a, s, mark_cb, &mk), "decode");
   }
-  const float *logits = logits_in;
-  if (!logits) {
-    mk("router");
-    MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
-    logits = b.logits;
-  }
   const bool shared = L->I_shared > 0 && L->shared_gate;
+  // the shared expert goes first, on the side stream where one exists (not
+  // when each kernel is timed: the marks time one stream)
+  SideStream *side = shared && !mk.m ? side_stream() : nullptr;
+  if (side) {
+    MOE_TRY(hip_check(hipEventRecord(side->fork, s), "fork"));
+    MOE_TRY(hip_check(hipStreamWaitEvent(side->s, side->fork, 0), "fork"));
+  }
+  int rc_sh = MOE_OK;
   if (shared) {
+    const hipStream_t ss = side ? side->s : s;
     const WView sg = bf16_view(L->shared_gate, L->I_shared, H);
     const WView su = bf16_view(L->shared_up, L->I_shared, H);
     const WView sd = bf16_view(L->shared_down, H, L->I_shared);
     if (skinny_supported(H, L->I_shared, T, sg, sd)) {
-      MOE_TRY(hip_check(launch_skinny_ffn(sg, su, sd, H, L->I_shared, T, x,
-                                          reinterpret_cast<uint16_t *>(b.a_sh), b.shared_y, s,
+      rc_sh = hip_check(launch_skinny_ffn(sg, su, sd, H, L->I_shared, T, x,
+                                          reinterpret_cast<uint16_t *>(b.a_sh), b.shared_y, ss,
                                           mark_cb, &mk, kSharedGemmNames),
-                        "shared skinny"));
+                        "shared skinny");
     } else if (use_gemm(T, H, L->I_shared, 1, T, true, MOE_FMT_BF16, MOE_FMT_BF16)) {
-      MOE_TRY(hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
+      rc_sh = hip_check(launch_gemm_ffn(sg, su, sd, H, L->I_shared, T, x, nullptr, nullptr, T,
                                         b.tiles_sh, reinterpret_cast<uint16_t *>(b.a_sh), nullptr,
-                                        b.shared_y, s, mark_cb, &mk, kSharedGemmNames),
-                        "shared gemm"));
+                                        b.shared_y, ss, mark_cb, &mk, kSharedGemmNames),
+                        "shared gemm");
     } else {
       mk("shared_gateup");
-      MOE_TRY(hip_check(
-          launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, s),
-          "shared gate/up"));
-      mk("shared_down");
-      MOE_TRY(hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, s),
-                        "shared down"));
+      rc_sh = hip_check(
+          launch_gateup_gemv(sg, su, H, L->I_shared, x, nullptr, T, nullptr, b.a_sh, ss),
+          "shared gate/up");
+      if (rc_sh == MOE_OK) {
+        mk("shared_down");
+        rc_sh = hip_check(launch_down_gemv(sd, H, L->I_shared, b.a_sh, nullptr, T, b.shared_y, ss),
+                          "shared down");
+      }
     }
   }
-  const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
-  if (fwd_small(L, T)) {
-    mk("select_plan");
-    MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, b.offsets,
-                                    b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
-                      "select"));
-    if (L->act_fmt == MOE_ACT_MXFP8) {
-      MOE_TRY(hip_check(launch_a8_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n, b.tiles,
-                                      b.a8, b.y_rows, s, mark_cb, &mk, kA8Names),
-                        "a8 ffn"));
-    } else if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt)) {
-      // several tokens: every selected expert's weights once, all its rows per load
-      MOE_TRY(hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n,
-                                        b.tiles, reinterpret_cast<uint16_t *>(b.a), b.x16,
-                                        b.y_rows, s, mark_cb, &mk, kRoutedGemmNames),
-                        "gemm ffn"));
-    } else {
+  if (side) {
+    // the caller's stream waits for the side stream only before the combine,
+    // but the join is recorded now, so that no path leaves the fork open
+    const int rc_j = hip_check(hipEventRecord(side->join, side->s), "join");
+    if (rc_sh == MOE_OK) rc_sh = rc_j;
+  }
+  auto join = [&]() -> int {
+    if (side) return hip_check(hipStreamWaitEvent(s, side->join, 0), "join");
+    return MOE_OK;
+  };
+  // the routed part on the caller's stream, up to the combine
+  auto routed = [&]() -> int {
+    const float *logits = logits_in;
+    if (!logits) {
+      mk("router");
+      MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
+      logits = b.logits;
+    }
+    const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);
+    if (fwd_small(L, T)) {
+      mk("select_plan");
+      MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, b.offsets,
+                                      b.sorted_token, nullptr, b.slot_pos, b.row_w, b.plan, s),
+                        "select"));
+      if (L->act_fmt == MOE_ACT_MXFP8)
+        return hip_check(launch_a8_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n, b.tiles,
+                                       b.a8, b.y_rows, s, mark_cb, &mk, kA8Names),
+                         "a8 ffn");
+      if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt))
+        // several tokens: every selected expert's weights once, all its rows per load
+        return hip_check(launch_gemm_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n,
+                                         b.tiles, reinterpret_cast<uint16_t *>(b.a), b.x16,
+                                         b.y_rows, s, mark_cb, &mk, kRoutedGemmNames),
+                         "gemm ffn");
       const int max_active = std::min(E, n);
       mk("routed_gateup");
       MOE_TRY(hip_check(
           launch_gateup_gemv(g, u, H, I, x, b.plan, max_active, b.sorted_token, b.a, s),
           "gate/up"));
       mk("routed_down");
-      MOE_TRY(hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down"));
+      return hip_check(launch_down_gemv(d, H, I, b.a, b.plan, max_active, b.y_rows, s), "down");
     }
-    mk("combine");
-    return hip_check(
-        launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
-        "combine");
-  }
-  mk("select");
-  MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
-                                  nullptr, nullptr, nullptr, nullptr, nullptr, s),
-                    "select"));
-  MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
-                                    b.slot_pos, b.dispatch_ws, s, mark_cb, &mk),
-                    "dispatch"));
-  MOE_TRY(run_ffn(T, H, I, x, g, u, d, L->act_fmt, b.offsets, b.sorted_token, n, b.y_rows, b.ffn,
-                  s, &mk));
+    mk("select");
+    MOE_TRY(hip_check(launch_select(L->route_mode, T, E, k, logits, token_ids, idx, w, nullptr,
+                                    nullptr, nullptr, nullptr, nullptr, nullptr, s),
+                      "select"));
+    MOE_TRY(hip_check(launch_dispatch(T, E, k, idx, b.offsets, b.sorted_token, b.sorted_slot,
+                                      b.slot_pos, b.dispatch_ws, s, mark_cb, &mk),
+                      "dispatch"));
+    return run_ffn(T, H, I, x, g, u, d, L->act_fmt, b.offsets, b.sorted_token, n, b.y_rows, b.ffn,
+                   s, &mk);
+  };
+  const int rc = rc_sh == MOE_OK ? routed() : rc_sh;
+  const int rc_join = join();  // on every path: no fork is left open
+  if (rc != MOE_OK) return rc;
+  if (rc_join != MOE_OK) return rc_join;
   mk("combine");
   return hip_check(
       launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
