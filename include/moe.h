@@ -186,12 +186,11 @@ int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_po
  * logits_in / token_ids: as in moe_route.  out_f32: fp32 [T][H];
  * out_bf16, topk_idx_out [T][k], topk_w_out [T][k]: optional outputs.
  * Above one token the shared expert runs on a second stream that the library
- * creates once per device (default priority, no memory), forked from
- * `stream` by an event before any other work and joined back before the
- * combine, so the call still orders after earlier work on `stream` and
- * before later work, and can be captured into a HIP graph from `stream`.
- * Calls from several host threads on one device share that stream: correct,
- * but their shared-expert kernels run one after another. */
+ * creates once per host thread and device (default priority, no memory, kept
+ * until the process ends), forked from `stream` by an event before any other
+ * work and joined back before the combine, so the call still orders after
+ * earlier work on `stream` and before later work, and can be captured into a
+ * HIP graph from `stream`. */
 size_t moe_forward_workspace(const moe_layer *layer, int T);
 int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,
                 const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,

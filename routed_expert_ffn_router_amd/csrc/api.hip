@@ -4,7 +4,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -133,23 +132,23 @@ struct Marker {
 
 void mark_cb(void *ctx, const char *name) { (*static_cast<Marker *>(ctx))(name); }
 
-// A second stream per device (default priority) with a fork and a join
-// event: the shared expert does not depend on the routing, so moe_forward runs
-// it there, beside the router, the selection, the dispatch and the routed
-// FFN, and joins before the combine.  Created once per device on first use;
-// null (everything on the caller's stream) if that fails.
+// A second stream (default priority) with a fork and a join event, per host
+// thread and device: the shared expert does not depend on the routing, so
+// moe_forward runs it there, beside the router, the selection, the dispatch
+// and the routed FFN, and joins before the combine.  Per thread, so that one
+// thread's graph capture never takes in another thread's work.  Created on
+// first use and kept until the process ends; null (everything on the
+// caller's stream) if that fails.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
+thread_local SideStream g_side[kMaxDevices];
 
 SideStream *side_stream() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream &ss = g_side[dev];
   if (!ss.s) {
     hipStream_t st = nullptr;
