@@ -717,8 +717,8 @@ __device__ __forceinline__ void fill_codebook(const int8_t *cb, uint2 *s_cb) {
 }
 
 // the same fill in two steps, so that the load can be issued early: thread t
-// loads entry t % 256 and later writes its copies t / 256, t / 256 + N / 256,
-// ... (N = the block's thread count, a multiple of 256)
+// loads entry t % 256 and later (codebook_entry_store_all) writes every copy
+// of it
 __device__ __forceinline__ uint32_t codebook_entry_load(const int8_t *cb) {
   return reinterpret_cast<const uint32_t *>(cb)[threadIdx.x & 255];
 }
@@ -734,18 +734,6 @@ __device__ __forceinline__ void codebook_entry_store_all(uint32_t w, uint2 *s_cb
   // bytes apart: the same copy for all lanes would hit one bank pair)
 #pragma unroll
   for (int j = 0; j < NC; j++) s_cb[e * NC + ((j + threadIdx.x) & (NC - 1))] = v;
-}
-template <int N>
-__device__ __forceinline__ void codebook_entry_store(uint32_t w, uint2 *s_cb) {
-  static_assert(N % 256 == 0, "thread count");
-  uint32_t b[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) b[j] = f32_to_bf16_bits((float)(int)(int8_t)((w >> (8 * j)) & 255u));
-  const uint2 v = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-  const int e = threadIdx.x & 255;
-#pragma unroll
-  for (int c = threadIdx.x >> 8; c < kNCopy; c += N / 256)
-    s_cb[e * kNCopy + ((c + e) & (kNCopy - 1))] = v;
 }
 
 // rows per wave step so the raw bits in flight stay near 32 dwords per lane
