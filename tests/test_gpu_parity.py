@@ -273,6 +273,9 @@ _DECODE_SHAPES = [
     ("h2048_e16_k6", 2048, 2048, 16, 6, "vq2", "vq2", "q2k", 2048),
     ("h2048_mxfp4", 2048, 2048, 12, 3, "mxfp4", "mxfp4", "mxfp4", 2048),
     ("h4096_bf16_down", 4096, 2048, 8, 2, "vq2", "vq2", "bf16", 2048),
+    # the other gate/up formats of the selection-and-gate/up launch, and VQ2 down
+    ("h2048_q2k_gateup", 2048, 2048, 8, 2, "q2k", "q2k", "q2k", 2048),
+    ("h2048_bf16_gateup_vq2_down", 2048, 2048, 8, 2, "bf16", "bf16", "vq2", 2048),
 ]
 _FMT = {"bf16": synth.FMT_BF16, "q2k": synth.FMT_Q2K, "vq2": synth.FMT_VQ2,
         "mxfp4": synth.FMT_MXFP4}
