@@ -659,7 +659,10 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
                    hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
                    const char *const names[4]) {
   const int E = offsets ? gate.E : 0;
-  const int max_tiles = ((n_rows + BM - 1) / BM + E + 7) / 8 * 8;
+  // tiles: sum over the active experts of ceil(rows / BM) <= n_rows / BM + the
+  // active count, which is at most min(E, n_rows) (blocks past the real count
+  // exit at once, but each still takes a slot and a load)
+  const int max_tiles = ((n_rows + BM - 1) / BM + std::min(E, n_rows) + 7) / 8 * 8;
   if (mark) mark(mark_ctx, names[0]);
   hipError_t err = launch(k_tile_list, dim3(1), dim3(1024), s, E, n_rows, BM, offsets, tiles);
   if (err != hipSuccess) return err;

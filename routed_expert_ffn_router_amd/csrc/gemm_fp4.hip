@@ -338,7 +338,10 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
                  hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
                  const char *const names[3]) {
   const int E = offsets ? gate.E : 0;
-  const int max_tiles = ((n_rows + BM - 1) / BM + E + 7) / 8 * 8;
+  // tiles: sum over the active experts of ceil(rows / BM) <= n_rows / BM + the
+  // active count, which is at most min(E, n_rows) (blocks past the real count
+  // exit at once, but each still takes a slot and a load)
+  const int max_tiles = ((n_rows + BM - 1) / BM + std::min(E, n_rows) + 7) / 8 * 8;
   if (mark) mark(mark_ctx, names[0]);
   hipError_t err = launch_tile_list(E, n_rows, BM, offsets, tiles, s);
   if (err != hipSuccess) return err;
