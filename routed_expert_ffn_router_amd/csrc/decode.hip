@@ -22,10 +22,11 @@ namespace moe {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kP1Threads = kDecThreads + 64;  // + the router wave
-// output rows per p3 block: 16 (two rounds of eight rows in flight per wave)
-// for the small Q2K/VQ2 chunks, 8 for MXFP4 and bf16
+// output rows per p3 block: 8 (two blocks per CU: four waves per SIMD keep
+// the VALU busy while rows arrive; with 16 rows and one block p3 took
+// 0.45 us longer), 16 for VQ2, whose blocks each fill the codebook
 template <int DFMT>
-constexpr int p3_rows() { return DFMT == MOE_FMT_Q2K || DFMT == MOE_FMT_VQ2 ? 16 : 8; }
+constexpr int p3_rows() { return DFMT == MOE_FMT_VQ2 ? 16 : 8; }
 constexpr int kP3Threads = kDecThreads;
 constexpr int kRouterChunks = 8;              // H <= 64 lanes x 8 bf16 x 8
 
