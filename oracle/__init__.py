@@ -77,6 +77,8 @@ def lib():
         L.orc_forward_a8.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp]
         L.orc_dense_masked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp]
         L.orc_mxfp8_quant.argtypes = [i32, i32, vp, vp, vp]
+        L.orc_a8_swiglu_codes.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp]
+        L.orc_a8_down.argtypes = [C.POINTER(Layer), vp, vp, vp, vp]
         L.orc_threads.restype = i32
         _lib = L
     return _lib
@@ -231,6 +233,33 @@ class LayerRef:
         if rc:
             raise ValueError("orc_forward failed")
         return out, idx, w
+
+    def a8_swiglu_codes(self, x, offsets, sorted_token):
+        """MX-FP8 codes [n_rows, I] and E8M0 scales [n_rows, I/32] of each bucket
+        row's SwiGLU output in the A8 variant (x quantized first)."""
+        x = _c(x, np.uint16)
+        offsets = _c(offsets, np.int32)
+        st = _c(sorted_token, np.int32)
+        n = int(offsets[-1])
+        codes = np.empty((n, self.I), np.uint8)
+        scales = np.empty((n, self.I // 32), np.uint8)
+        rc = lib().orc_a8_swiglu_codes(C.byref(self.c), x.shape[0], _p(x), _p(offsets), _p(st),
+                                       _p(codes), _p(scales))
+        if rc:
+            raise ValueError("orc_a8_swiglu_codes failed")
+        return codes, scales
+
+    def a8_down(self, offsets, codes, scales):
+        """y_rows [n_rows, H]: each bucket row's down projection of the given
+        MX-FP8 codes and scales."""
+        offsets = _c(offsets, np.int32)
+        codes = _c(codes, np.uint8)
+        scales = _c(scales, np.uint8)
+        y = np.empty((int(offsets[-1]), self.H), np.float32)
+        rc = lib().orc_a8_down(C.byref(self.c), _p(offsets), _p(codes), _p(scales), _p(y))
+        if rc:
+            raise ValueError("orc_a8_down failed")
+        return y
 
     def dense_masked(self, x, idx, w):
         x = _c(x, np.uint16)

@@ -346,11 +346,15 @@ static void swiglu(int H, int I, const double *x, const float *Wg, const float *
   }
 }
 
-/* the same, with the activations entering each projection passed through
- * MX-FP8 quantization (used by the A8 variant) */
+/* The A8 variant in its two stages: gate/up on the MX-FP8 projection of x,
+ * whose SwiGLU output is itself quantized to MX-FP8 (codes + E8M0 scales),
+ * then down on the decoded codes.  Each MX-FP8 rounding is the OCP MX v1.0
+ * rule of mx8_group below. */
+static unsigned mx8_group(const double *v, int n, uint8_t *codes);
 static void mx8_round(int K, double *v);
-static void swiglu_a8(int H, int I, const double *x, const float *Wg, const float *Wu,
-                      const float *Wd, double *a, double *y) {
+
+static void a8_gateup(int H, int I, const double *x, const float *Wg, const float *Wu,
+                      double *a, uint8_t *codes, uint8_t *scales) {
   double *xq = (double *)malloc((size_t)H * sizeof(double));
   memcpy(xq, x, (size_t)H * sizeof(double));
   mx8_round(H, xq);
@@ -363,14 +367,35 @@ static void swiglu_a8(int H, int I, const double *x, const float *Wg, const floa
     }
     a[i] = silu(g) * u;
   }
-  mx8_round(I, a);
+  for (int g = 0; g < I; g += 32)
+    scales[g / 32] = (uint8_t)mx8_group(a + g, (I - g) < 32 ? (I - g) : 32, codes + g);
+  free(xq);
+}
+
+/* a = E4M3(codes) * 2^(scale - 127), per 32 along I */
+static void mx8_decode(int I, const uint8_t *codes, const uint8_t *scales, double *a) {
+  for (int i = 0; i < I; i++) a[i] = (double)orc_e4m3(codes[i]) * orc_e8m0(scales[i / 32]);
+}
+
+static void down_d(int H, int I, const double *a, const float *Wd, double *y) {
 #pragma omp parallel for schedule(static)
   for (int n = 0; n < H; n++) {
     double acc = 0.0;
     for (int i = 0; i < I; i++) acc += a[i] * (double)Wd[(int64_t)n * I + i];
     y[n] = acc;
   }
-  free(xq);
+}
+
+/* the SwiGLU expert with the activations entering each projection passed
+ * through MX-FP8 quantization */
+static void swiglu_a8(int H, int I, const double *x, const float *Wg, const float *Wu,
+                      const float *Wd, double *a, double *y) {
+  uint8_t *codes = (uint8_t *)malloc((size_t)I + 32);
+  uint8_t *scales = (uint8_t *)malloc((size_t)I / 32 + 2);
+  a8_gateup(H, I, x, Wg, Wu, a, codes, scales);
+  mx8_decode(I, codes, scales, a);
+  down_d(H, I, a, Wd, y);
+  free(codes), free(scales);
 }
 
 typedef struct {
@@ -438,6 +463,61 @@ int orc_expert_ffn(const orc_layer *L, int T, const uint16_t *x, const int32_t *
   int rc = expert_rows_d(L, T, x, offsets, sorted_token, y, 0);
   for (int64_t i = 0; i < rows * L->H; i++) y_rows[i] = (float)y[i];
   free(y);
+  return rc;
+}
+
+/* The A8 variant's intermediate: for every bucket row r, the MX-FP8 codes
+ * [I] and E8M0 scales [I/32] of the SwiGLU output of its expert on the
+ * MX-FP8 projection of its token (the first stage of swiglu_a8). */
+int orc_a8_swiglu_codes(const orc_layer *L, int T, const uint16_t *x, const int32_t *offsets,
+                        const int32_t *sorted_token, uint8_t *codes, uint8_t *scales) {
+  if (check_layer(L) || L->I % 32) return -1;
+  int H = L->H, I = L->I;
+  double *xd = (double *)malloc((size_t)H * sizeof(double));
+  double *a = (double *)malloc((size_t)I * sizeof(double));
+  int rc = 0;
+  (void)T;
+  for (int e = 0; e < L->E && rc == 0; e++) {
+    if (offsets[e + 1] == offsets[e]) continue;
+    expert_w w;
+    if (load_expert(L, e, &w)) {
+      rc = -1;
+      break;
+    }
+    for (int r = offsets[e]; r < offsets[e + 1]; r++) {
+      token_x(H, x, sorted_token[r], xd);
+      a8_gateup(H, I, xd, w.g, w.u, a, codes + (int64_t)r * I, scales + (int64_t)r * (I / 32));
+    }
+    free_expert(&w);
+  }
+  free(xd), free(a);
+  return rc;
+}
+
+/* The A8 variant's second stage on given codes: y_rows[r] = Wd_e a_r with
+ * a_r decoded from codes[r], scales[r] (fp64 accumulation, rounded once). */
+int orc_a8_down(const orc_layer *L, const int32_t *offsets, const uint8_t *codes,
+                const uint8_t *scales, float *y_rows) {
+  if (check_layer(L) || L->I % 32) return -1;
+  int H = L->H, I = L->I;
+  double *a = (double *)malloc((size_t)I * sizeof(double));
+  double *y = (double *)malloc((size_t)H * sizeof(double));
+  int rc = 0;
+  for (int e = 0; e < L->E && rc == 0; e++) {
+    if (offsets[e + 1] == offsets[e]) continue;
+    float *wd = dequant_all(&L->down, e);
+    if (!wd) {
+      rc = -1;
+      break;
+    }
+    for (int r = offsets[e]; r < offsets[e + 1]; r++) {
+      mx8_decode(I, codes + (int64_t)r * I, scales + (int64_t)r * (I / 32), a);
+      down_d(H, I, a, wd, y);
+      for (int n = 0; n < H; n++) y_rows[(int64_t)r * H + n] = (float)y[n];
+    }
+    free(wd);
+  }
+  free(a), free(y);
   return rc;
 }
 

@@ -99,6 +99,15 @@ void orc_mxfp8_quant(int rows, int K, const float *in, uint8_t *codes, uint8_t *
 int orc_forward_a8(const orc_layer *L, int T, const uint16_t *x, const float *logits_in,
                    const int64_t *token_ids, float *out, int32_t *idx, float *w);
 
+/* its two stages over bucket rows (offsets/sorted_token as for
+ * orc_expert_ffn; I % 32 == 0): the MX-FP8 codes [n_rows][I] and E8M0
+ * scales [n_rows][I/32] of each row's SwiGLU output, and the down projection
+ * of given codes, y_rows [n_rows][H] */
+int orc_a8_swiglu_codes(const orc_layer *L, int T, const uint16_t *x, const int32_t *offsets,
+                        const int32_t *sorted_token, uint8_t *codes, uint8_t *scales);
+int orc_a8_down(const orc_layer *L, const int32_t *offsets, const uint8_t *codes,
+                const uint8_t *scales, float *y_rows);
+
 int orc_threads(void);
 
 #ifdef __cplusplus

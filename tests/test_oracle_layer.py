@@ -188,3 +188,127 @@ def test_a8_forward_close_to_plain_forward():
     assert np.array_equal(idx, idx8)
     err = _normwise(out8, out.astype(np.float64))
     assert 1e-4 < err < 0.1
+
+
+# --------------------------------------------------------------------------
+# the A8 variant's two quantization points, pinned against hand-derived
+# values: torch's E4M3 conversion and the OCP MX scale rule written out here
+# --------------------------------------------------------------------------
+
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _mx8_torch(v):
+    """OCP MX-FP8 of fp64 values per 32 along the last axis, by hand: scale
+    2^(floor(log2 amax) - 8), elements through torch's float8_e4m3fn cast
+    (ties to even) after clamping to +-448 (the MX rule saturates)."""
+    g = v.reshape(*v.shape[:-1], -1, 32)
+    amax = np.abs(g).max(-1, keepdims=True)
+    s = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    y = np.clip(g / np.exp2(s), -448, 448)
+    q = torch.from_numpy(y).to(torch.float8_e4m3fn).double().numpy()
+    return (q * np.exp2(s)).reshape(v.shape)
+
+
+def _mxfp4_matrix(vals):
+    """An MXFP4 projection [1, N, K] holding exactly `vals` (each entry an
+    E2M1 value times the power of two of its group of 32, zeros elsewhere)."""
+    N, K = vals.shape
+    nib = np.zeros((N, K), np.uint8)
+    sc = np.full((N, K // 32), 127, np.uint8)
+    for n in range(N):
+        for g in range(K // 32):
+            grp = vals[n, 32 * g:32 * g + 32]
+            nz = grp[grp != 0]
+            e = 0 if nz.size == 0 else int(np.floor(np.log2(np.abs(nz).max() / 6.0)) + 1)
+            sc[n, g] = 127 + e
+            for i, v in enumerate(grp):
+                m = abs(v) / 2.0 ** e
+                c = _E2M1.index(m)
+                nib[n, 32 * g + i] = c | (8 if v < 0 else 0)
+    data = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return synth.Proj(synth.FMT_MXFP4, 1, N, K, data.reshape(1, N, K // 2), sc.reshape(1, N, K // 32))
+
+
+def _one_hot_a8_layer():
+    """E = 1, k = 1, H = I = 64, MXFP4 weights, no shared expert: the token
+    e_0 picks column 0 of gate and up, so g_i = G[i], u_i = U[i] exactly, and
+    the down projection is the identity, so the layer's output is the
+    SwiGLU output after its MX-FP8 rounding."""
+    H = I = 64
+    rng = np.random.default_rng(21)
+    Gv = np.array([_E2M1[1 + i % 7] * (-1) ** (i // 7) * 2.0 ** (i % 5 - 2) for i in range(I)])
+    Uv = np.array([_E2M1[1 + (3 * i) % 7] * (-1) ** i * 2.0 ** ((i // 32) * 3 - 1) for i in range(I)])
+    G = np.zeros((I, H))
+    U = np.zeros((I, H))
+    G[:, 0], U[:, 0] = Gv, Uv
+    spec = synth.LayerSpec("onehot", H, I, 1, 1, synth.FMT_MXFP4, synth.FMT_MXFP4,
+                           synth.FMT_MXFP4, 0)
+    L = synth.Layer(spec, synth.gen_bf16(rng, (1, H), 0.1), _mxfp4_matrix(G), _mxfp4_matrix(U),
+                    _mxfp4_matrix(np.eye(H)), None, None, None, None)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0] = 0x3F80  # 1.0: its MX-FP8 projection is itself
+    return L, x, Gv, Uv
+
+
+def test_a8_swiglu_output_quantized_one_hot():
+    L, x, g, u = _one_hot_a8_layer()
+    R = oracle.LayerRef(L)
+    assert np.array_equal(oracle.dequant_matrix(L.gate)[:, 0], g)
+    assert np.array_equal(oracle.dequant_matrix(L.down), np.eye(64))
+    a = g / (1.0 + np.exp(-g)) * u
+    want = _mx8_torch(a)
+    out, idx, w = R.forward(x, a8=True)
+    assert idx[0, 0] == 0 and w[0, 0] == 1.0
+    assert np.array_equal(out[0].astype(np.float64), want)
+    # the rounding is visible: without it the output would be fp32(a)
+    assert (out[0] != a.astype(np.float32)).sum() > 32
+    # the plain layer keeps a
+    plain, _, _ = R.forward(x)
+    np.testing.assert_allclose(plain[0], a, rtol=1e-6)
+    # the first stage alone gives the same codes
+    off, st, _, _ = oracle.dispatch(idx, 1)
+    codes, scales = R.a8_swiglu_codes(x, off, st)
+    dec = np.array([oracle.e4m3(c) for c in codes[0]]) * np.repeat(
+        [oracle.e8m0(s) for s in scales[0]], 32)
+    assert np.array_equal(dec, want)
+
+
+def test_a8_forward_invariant_under_token_requantization():
+    """The tokens enter gate/up through their MX-FP8 projection: replacing x
+    by that projection (computed here with torch) changes nothing in the A8
+    layer, while the plain layer sees the difference."""
+    spec = _spec(H=512, I=256, E=4, k=2, fg=3, fu=3, fd=3, Is=0)
+    L = synth.gen_layer(spec, 13)
+    R = oracle.LayerRef(L)
+    x = synth.gen_x(512, 5, 14)
+    xv = _x64(x).numpy()
+    xq = _mx8_torch(xv)
+    xq_bits = synth.f32_to_bf16_bits(xq.astype(np.float32))
+    assert np.array_equal(_x64(xq_bits).numpy(), xq)  # exact in bf16
+    assert not np.array_equal(xq, xv)
+    lg = np.random.default_rng(15).standard_normal((5, 4)).astype(np.float32)
+    a, ia, wa = R.forward(x, logits_in=lg, a8=True)
+    b, ib, wb = R.forward(xq_bits, logits_in=lg, a8=True)
+    assert np.array_equal(ia, ib) and np.array_equal(wa, wb)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    p, _, _ = R.forward(x, logits_in=lg)
+    q, _, _ = R.forward(xq_bits, logits_in=lg)
+    assert _normwise(p, q.astype(np.float64)) > 1e-3
+
+
+def test_a8_stages_compose_to_forward():
+    """codes -> down -> combine equals the A8 forward (the fp32 rounding of the
+    rows is the only difference)."""
+    spec = _spec(H=512, I=256, E=4, k=2, fg=3, fu=3, fd=3, Is=256)
+    L = synth.gen_layer(spec, 16)
+    R = oracle.LayerRef(L)
+    x = synth.gen_x(512, 6, 17)
+    out, idx, w = R.forward(x, a8=True)
+    off, st, _, sp = oracle.dispatch(idx, 4)
+    codes, scales = R.a8_swiglu_codes(x, off, st)
+    y = R.a8_down(off, codes, scales)
+    ref = oracle.combine(y, sp, w, R.shared_ffn(x))
+    assert _normwise(ref, out.astype(np.float64)) < 1e-6
+    # and differs from the plain layer's rows by the MX-FP8 effect
+    assert _normwise(y, R.expert_ffn(x, off, st).astype(np.float64)) > 1e-3

@@ -241,10 +241,38 @@ def test_hash_routing_closed_form():
 
 
 def test_hash_routing_wraps_mod_E():
-    z = oracle.splitmix64(129279)
+    # worked out by hand from the definition: splitmix64(129279) =
+    # 0x269DD7175F5319FF, low byte 0xFF = 255, so the k = 8 consecutive
+    # experts wrap past E - 1 to 0
     E, k = 256, 8
     idx, _ = oracle.select_hash(np.array([129279], np.int64), np.zeros((1, E), np.float32), k)
-    assert list(idx[0]) == [(z % E + j) % E for j in range(k)]
+    assert list(idx[0]) == [255, 0, 1, 2, 3, 4, 5, 6]
+    assert oracle.splitmix64(129279) == 0x269DD7175F5319FF
+
+
+def test_topk_nan_ranks_as_minus_inf():
+    """NaN ranks as -inf: never ahead of a finite logit, tied with -inf (the
+    lower index first), and its weight is exp(-inf) = 0."""
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    logits = np.array([[nan, 1.0, nan, 0.0],
+                       [nan, -inf, 2.0, nan],
+                       [-inf, nan, nan, nan]], np.float32)
+    idx, w = oracle.select_topk(logits, 3)
+    assert list(idx[0]) == [1, 3, 0]
+    assert list(idx[1]) == [2, 0, 1]
+    assert list(idx[2]) == [0, 1, 2]
+    e = math.e
+    np.testing.assert_allclose(w[0], [e / (e + 1), 1 / (e + 1), 0.0], rtol=1e-7, atol=0)
+    assert list(w[1]) == [1.0, 0.0, 0.0]
+    # brute force: a stable descending sort with NaN replaced by -inf
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((40, 16)).astype(np.float32)
+    lg[rng.random((40, 16)) < 0.3] = np.nan
+    lg[rng.random((40, 16)) < 0.1] = -np.inf
+    idx, w = oracle.select_topk(lg, 6)
+    ref = np.argsort(-np.where(np.isnan(lg), -np.inf, lg), axis=1, kind="stable")[:, :6]
+    assert np.array_equal(idx, ref)
+    assert not np.isnan(w).any()
 
 
 # --------------------------------------------------------------------------
