@@ -48,9 +48,13 @@ def _args():
     ap.add_argument("--marked-steps", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extras", default="prefill_2048",
+    ap.add_argument("--extras", default="prefill_2048,decode_b16_zipf,verify_t6,verify_t96_zipf,"
+                    "mxfp4_decode_b1,mxfp4_hash_decode_b1,mxfp4_a8_prefill_4096",
                     help="comma-separated extra workloads measured after the headline")
-    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--extra-warmup", type=int, default=20)
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the HBM / matrix-core peak probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 4 times (HBM counter calibration) and exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -254,6 +258,9 @@ def step_flops(L, T):
 # setup
 # --------------------------------------------------------------------------
 
+_LAYERS = {}  # LayerSpec -> (host layer, device replicas): one per spec for the whole run
+
+
 def setup(wname, replicas, seed, npool, dev):
     import torch
 
@@ -261,9 +268,17 @@ def setup(wname, replicas, seed, npool, dev):
     import synth
 
     w = synth.WORKLOADS[wname]
-    host = synth.gen_layer(w.layer, seed)
-    base = moe.DeviceLayer.upload(host, route_mode=w.route, device=dev, act=w.act)
-    layers = [base] + [base.clone() for _ in range(replicas - 1)]
+    if w.layer not in _LAYERS:
+        for spec in list(_LAYERS):  # one layer family in device memory at a time
+            if spec != w.layer:
+                del _LAYERS[spec]
+        torch.cuda.empty_cache()
+        host = synth.gen_layer(w.layer, seed)
+        _LAYERS[w.layer] = (host, [moe.DeviceLayer.upload(host, device=dev)])
+    host, reps = _LAYERS[w.layer]
+    while len(reps) < replicas:
+        reps.append(reps[0].clone())
+    layers = [r.with_route_mode(w.route).with_act(w.act) for r in reps[:replicas]]
     xs, lgs, tids = [], [], []
     for i in range(npool):
         x, lg, ti = synth.gen_step_inputs(w, seed, step=i)
@@ -285,7 +300,10 @@ def unique_experts(f, layers, xs, lgs, tids, n=8):
 
 
 def time_steps(f, layers, xs, lgs, tids, steps, warmup, graph_steps, use_graph):
-    """Seconds per step over exactly `steps` steps."""
+    """Seconds per step: the median over the timed steps (graph replays of G
+    steps each: the median replay over G) of exactly `steps` steps, every one
+    bracketed by a pair of events on the stream it runs on, the whole timed
+    region by synchronisation."""
     import torch
 
     R, P = len(layers), len(xs)
@@ -315,26 +333,26 @@ def time_steps(f, layers, xs, lgs, tids, steps, warmup, graph_steps, use_graph):
         if not torch.equal(gout, f.out):
             raise RuntimeError("graph replay differs from eager execution")
         reps = steps // G
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
+        for a, b in ev:
+            a.record()
             g.replay()
-        t1.record()
+            b.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / 1e3 / steps, G
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3 / G, G
     for i in range(warmup):
         run(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
+    for i, (a, b) in enumerate(ev):
+        a.record()
         run(i)
-    t1.record()
+        b.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / 1e3 / steps, 1
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3, 1
 
 
 def kernel_times(f, layers, xs, lgs, tids, steps):
@@ -363,42 +381,118 @@ def kernel_times(f, layers, xs, lgs, tids, steps):
         for j, name in enumerate(names):
             a, b = evs[i][j]
             acc.setdefault(name, []).append(a.elapsed_time(b) / 1e3)
-    return {k: float(np.mean(v[1:] if len(v) > 2 else v)) for k, v in acc.items()}
+    return {k: float(np.median(v[1:] if len(v) > 2 else v)) for k, v in acc.items()}
 
 
-def cpu_baseline(host, w, seed, budget_s):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(host, w, seed, budget_s, max_tokens=None):
+    """The oracle (route, dequantize the selected experts, fp64 FFNs, combine)
+    on the host: on all its threads for about budget_s, and single-threaded
+    for about a third of that.  Decode workloads run whole steps; a prefill
+    chunk runs a bounded sample of max_tokens of its tokens per call (tokens
+    are independent: no capacity limit)."""
     import oracle
     import synth
 
     R = oracle.LayerRef(host, route_mode=w.route)
-    n, t_total = 0, 0.0
-    while n < 2 or (t_total < budget_s and n < 1000):
-        x, lg, ti = synth.gen_step_inputs(w, seed, step=10_000 + n)
-        t0 = time.perf_counter()
-        R.forward(x, lg, ti)
-        t_total += time.perf_counter() - t0
-        n += 1
-    return {"value": n * w.T / t_total, "unit": "tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"{n} steps of {w.name} (T={w.T}) through the full oracle layer "
-                      f"(route, dequantize the selected experts, fp64 FFNs, combine); "
-                      f"{t_total:.1f} s"}
+    all_threads = oracle.threads()
+
+    def run(threads, budget):
+        oracle.set_threads(threads)
+        n, t_total = 0, 0.0
+        while n < 1 or (t_total < budget and n < 1000):
+            x, lg, ti = synth.gen_step_inputs(w, seed, step=10_000 + n)
+            if max_tokens is not None:
+                x = x[:max_tokens]
+                lg = None if lg is None else lg[:max_tokens]
+                ti = None if ti is None else ti[:max_tokens]
+            t0 = time.perf_counter()
+            R.forward(x, lg, ti)
+            t_total += time.perf_counter() - t0
+            n += 1
+        return n, n * x.shape[0] / t_total, t_total
+
+    n, v, t = run(all_threads, budget_s)
+    n1, v1, t1 = run(1, budget_s / 3)
+    oracle.set_threads(all_threads)
+    what = (f"{w.name} (T={w.T})" if max_tokens is None else
+            f"the first {max_tokens} tokens of {w.name} chunks (T={w.T})")
+    return {"value": v, "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"{n} calls on {what} through the full oracle layer (route, dequantize "
+                      f"the selected experts, fp64 FFNs, combine); {t:.1f} s",
+            "single_thread": {"value": v1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} calls, {t1:.1f} s"},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def probe_peaks(dev):
+    """Achievable peaks on this GPU: a streaming read of 4 GiB (16 times the
+    last-level cache) and dense matrix-instruction loops on every CU."""
+    import torch
+
+    import routed_expert_ffn_router_amd as moe
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts[1:])
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(moe.probe_sink_words(nbytes), dtype=torch.int32, device=dev)
+    t = timed(lambda: moe.probe_hbm_read(buf, sink), 6)
+    out = {"hbm_read_gbps": nbytes / t / 1e9}
+    del buf, sink
+    blocks, iters = 256 * 8, 400
+    sink = torch.empty(blocks * 256 * 32, dtype=torch.float32, device=dev)
+    for name, kind in (("mfma_bf16_tflops", moe.PROBE_BF16), ("mfma_f16_tflops", moe.PROBE_F16),
+                       ("mfma_bf16_32x32_tflops", moe.PROBE_BF16_32),
+                       ("mfma_f16_32x32_tflops", moe.PROBE_F16_32),
+                       ("mfma_f8f4_tflops", moe.PROBE_F8F4)):
+        fl = []
+        t = timed(lambda: fl.append(moe.probe_mfma(kind, blocks, iters, sink)), 4)
+        out[name] = fl[0] / t / 1e12
+    del sink
+    torch.cuda.empty_cache()
+    out["method"] = ("moe_probe_hbm_read over 4 GiB (best of 5 launches); moe_probe_mfma, "
+                     f"{blocks} workgroups x 4 waves x {iters} rounds of 8 independent "
+                     "instructions (best of 3)")
+    return out
 
 
 def measure(wname, args, dev, headline):
     import routed_expert_ffn_router_amd as moe
 
-    w, host, layers, xs, lgs, tids = setup(wname, args.replicas if headline else 2, 0,
-                                           64 if w_is_decode(wname) else 4, dev)
+    # decode steps touch ~0.1 GB of a replica: rotating over all replicas keeps
+    # the 256 MB last-level cache from serving the shared expert and router
+    w, host, layers, xs, lgs, tids = setup(
+        wname, args.replicas if headline or w_is_decode(wname) else 2, 0,
+        64 if w_is_decode(wname) else 4, dev)
     L = layers[0]
     f = moe.Forward(L, w.T, dev)
     U = unique_experts(f, layers, xs, lgs, tids)
     decode = w_is_decode(wname)
     steps = args.steps if headline else args.extra_steps
-    warm = args.warmup if headline else 1
+    warm = args.warmup if headline else args.extra_warmup
     sec, G = time_steps(f, layers, xs, lgs, tids, steps, warm, args.graph_steps,
                         decode and not args.no_graph)
-    kt = kernel_times(f, layers, xs, lgs, tids, args.marked_steps if headline else 3)
+    kt = kernel_times(f, layers, xs, lgs, tids, args.marked_steps if headline else 10)
     res = {"workload": wname, "T": w.T, "sec_per_step": sec, "tokens_per_s": w.T / sec,
            "unique_experts": U, "graph_steps": G,
            "hbm_bytes_per_step": step_bytes(L, w.T, U),
@@ -431,6 +525,20 @@ def measure(wname, args, dev, headline):
     return res, host, w, L
 
 
+def add_probed(roof, peaks):
+    """Beside the spec peak: the probed one and the fraction of it."""
+    if not peaks:
+        return
+    if roof["unit"] == "GB/s":
+        p = peaks["hbm_read_gbps"]
+    elif roof["kernel"].startswith("a8_"):
+        p = peaks["mfma_f8f4_tflops"]
+    else:  # the faster of the fp16 shapes: what this chip's matrix cores can give
+        p = max(peaks["mfma_f16_tflops"], peaks["mfma_f16_32x32_tflops"])
+    roof["peak_probed"] = p
+    roof["frac_probed"] = roof["achieved"] / p
+
+
 def w_is_decode(wname):
     import synth
     return synth.WORKLOADS[wname].T <= 64
@@ -452,13 +560,19 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    peaks = None if args.no_probes else probe_peaks(dev)
     head, host, w, L = measure(args.workload, args, dev, True)
     roof = head["roofline"]
     roof["traffic"] = measured_traffic(args.workload, roof["kernel"])
+    add_probed(roof, peaks)
     extras = {}
     for name in [e for e in args.extras.split(",") if e and e != args.workload]:
         torch.cuda.empty_cache()
-        r, _, _, _ = measure(name, args, dev, False)
+        r, xhost, xw, _ = measure(name, args, dev, False)
+        r["roofline"]["traffic"] = measured_traffic(name, r["roofline"]["kernel"])
+        add_probed(r["roofline"], peaks)
+        if not args.no_cpu_baseline and xw.T >= 2048:
+            r["cpu_baseline"] = cpu_baseline(xhost, xw, 0, args.cpu_seconds / 2, max_tokens=32)
         extras[name] = r
     cpu = None
     if not args.no_cpu_baseline:
@@ -487,6 +601,7 @@ def main():
         "kernels": head["kernels"],
         "roofline": roof,
         "cpu_baseline": cpu,
+        "probed_peaks": peaks,
         "extras": extras,
     }
     print(json.dumps(line), flush=True)

@@ -26,6 +26,18 @@
  *    reported by these calls.
  *  - T == 0 (no tokens) is a valid no-op.
  *  - Calls are reentrant; concurrent calls must use distinct ws buffers.
+ *    The library holds no mutable state of its own and creates no HIP
+ *    objects: every stream and event it uses is the caller's.
+ *
+ * Value ranges (preconditions the host cannot check without reading device
+ * memory; outside them results may be inf/NaN where the CPU reference is
+ * finite).  The matrix-core paths (moe_expert_ffn / moe_forward from four
+ * tokens on, VQ2 or Q2K gate/up or any down projection) and the one-token
+ * down projection of Q2K and MXFP4 experts round the following to IEEE
+ * binary16, so each must stay below 65504 in magnitude: the bf16 tokens
+ * (VQ2 and Q2K gate/up), the SwiGLU output, each dequantized VQ2 and Q2K
+ * weight and the Q2K terms d*scale and dmin*min.  Values below 2^-14 become
+ * binary16 subnormals: an absolute error of at most 2^-25 each.
  */
 #ifndef LIBMOE_MOE_H
 #define LIBMOE_MOE_H
@@ -37,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum {
   MOE_OK = 0,
@@ -97,18 +109,40 @@ typedef struct {
  *                 quantization": the MXFP4 variant keeps the released FP4
  *                 experts.) */
 enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP8 = 1 };
+/* moe_expert_ffn only: MOE_ACT_MXFP8 | MOE_ACT_TRACE also leaves the fp32
+ * SwiGLU output, before its MX-FP8 quantization, in the workspace (see
+ * moe_expert_ffn_a8_layout), for tests of the quantizer on the values the
+ * matrix cores produced. */
+#define MOE_ACT_TRACE 0x100
 
 /* One MoE FFN layer.  gate/up are [E][I][H], down is [E][H][I]; the shared
  * expert (optional: NULL pointers or I_shared == 0) is bf16 [I_shared][H],
  * [I_shared][H], [H][I_shared]; the router is bf16 [E][H].  act_fmt: a
- * MOE_ACT_* value for the routed experts (the shared expert is always bf16). */
+ * MOE_ACT_* value for the routed experts (the shared expert is always bf16).
+ * steer_dir: optional fp32 [H] direction added to the layer's output with
+ * strength steer_alpha (see moe_combine); NULL for none. */
 typedef struct {
   int32_t H, I, E, k, I_shared, route_mode;
   const uint16_t *w_router;
   moe_weights gate, up, down;
   const uint16_t *shared_gate, *shared_up, *shared_down;
   int32_t act_fmt;
+  const float *steer_dir;
+  float steer_alpha;
 } moe_layer;
+
+/* A second stream for moe_forward, owned by the caller: `stream` (a
+ * hipStream_t, default priority) runs the shared expert beside the routed
+ * work; `fork` and `join` are hipEvent_t (timing may be disabled) that the
+ * call records -- fork on the caller's stream before anything else, join on
+ * `stream` after the shared expert -- and waits on (the caller's stream
+ * waits for join before the combine).  Concurrent calls need distinct
+ * moe_side_stream objects. */
+typedef struct {
+  void *stream;
+  void *fork;
+  void *join;
+} moe_side_stream;
 
 /* Text of the last error on the calling thread ("" if none). */
 const char *moe_last_error(void);
@@ -118,7 +152,17 @@ int moe_abi_version(void);
 /* moe_route: router logits + expert selection.
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h], every product exact and
  *   the sum accumulated in fp64, rounded once to fp32 (the router stays at
- *   full precision).  Then MOE_ROUTE_SOFTMAX_TOPK or MOE_ROUTE_HASH selection.
+ *   full precision: dibi8.com ds4 guide, "Cac Doi Moi Kien Truc Chinh" item
+ *   1).  Then MOE_ROUTE_SOFTMAX_TOPK or MOE_ROUTE_HASH selection.
+ * Exactness domain: the kernels sum in other orders than h = 0, 1, ...; the
+ *   result equals the h-order fp64 sum bit for bit whenever that sum is exact
+ *   in fp64, in any order -- it is when sum_h |x_h w_h| is below 2^53 times
+ *   the last bit of the smallest nonzero product, e.g. when every nonzero x
+ *   and router weight has magnitude >= 2^-14 and sum_h |x_h w_h| < 2^11 --
+ *   and so the selected experts are reproducible.  Outside it
+ *   the fp64 sums may differ in their last bits, which changes the fp32
+ *   logit only when it lies within 2^-29 relative of an fp32 rounding
+ *   boundary.
  * x: bf16 [T][H]; w_router: bf16 [E][H].
  * logits_in: optional fp32 [T][E]; when given, the router GEMM is skipped
  *   and these logits are used (x and w_router may then be NULL).
@@ -134,7 +178,12 @@ int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uin
 
 /* ---------------------------------------------------------------------- */
 /* moe_dispatch: bucket the T*k (token, choice) slots by expert, stable in
- * slot order f = t*k + j (a counting sort by prefix sum):
+ * slot order f = t*k + j (a counting sort by prefix sum).  The pages route
+ * each token to k routed experts (dibi8.com ds4 guide, "Cac Doi Moi Kien
+ * Truc Chinh" item 1; grapeot.me ds4 post, opening paragraphs, for hash
+ * routing) but describe no bucketing: this grouping of the slots by expert
+ * is the library's own, so that each expert's weights are read once for all
+ * of its tokens:
  *   expert_offsets[e] = number of slots routed to experts < e
  *   (expert_offsets[E] = T*k); bucket e is rows [offsets[e], offsets[e+1])
  *   listing its slots in ascending f:
@@ -150,7 +199,10 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
 /* moe_expert_ffn: SwiGLU FFN of each expert over its bucket of tokens:
  *   for bucket row r of expert e, token t = sorted_token[r]:
  *   y_rows[r] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),
- * with the weights dequantized on the fly.  x: bf16 [T][H]; gate/up/down
+ * with the weights dequantized on the fly (routed experts in 2-bit formats,
+ * up/gate IQ2_XXS-class and down Q2_K: dibi8.com ds4 guide, "Cac Doi Moi
+ * Kien Truc Chinh" item 1; MXFP4 experts: hysenlabs.com ds4 page, "Model
+ * support and quantization"; the SwiGLU form is the library's reading).  x: bf16 [T][H]; gate/up/down
  * as in moe_layer (any of the formats; gate and up of one format).
  * expert_offsets: int32 [E+1] and sorted_token: int32 [n_rows] from
  *   moe_dispatch; expert_offsets == NULL means one dense expert (expert 0
@@ -164,19 +216,37 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
  * FP4 matrix instructions. */
 size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
                                 int fmt_down, int act_fmt);
+/* Where a MOE_ACT_MXFP8 call of moe_expert_ffn with these sizes leaves the
+ * quantized SwiGLU output in its workspace: byte offsets of the E4M3 codes
+ * uint8 [n_rows][I] and of their E8M0 scales uint8 [n_rows][I/32] (bucket
+ * order), and, with MOE_ACT_TRACE, of the fp32 values they were quantized
+ * from, fp32 [n_rows][I]; valid until the workspace is reused.  For tests
+ * that compare the MX-FP8 intermediate with a reference. */
+int moe_expert_ffn_a8_layout(int T, int n_rows, int E, int H, int I, size_t *codes_off,
+                             size_t *scales_off, size_t *f32_off);
 int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
                    const moe_weights *up, const moe_weights *down, int act_fmt,
                    const int32_t *expert_offsets, const int32_t *sorted_token, int n_rows,
                    float *y_rows, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
-/* moe_combine: the gather form of the weighted scatter-add:
+/* moe_combine: the gather form of the weighted scatter-add, then the
+ * optional steering term:
  *   out[t][n] = shared_y[t][n] + sum_j topk_w[t][j] * y_rows[slot_pos[t*k+j]][n]
- * summed in j order in fp32.  shared_y: optional fp32 [T][H].
+ *               + steer_alpha * steer_dir[n]
+ * accumulated in fp64 in that order (each product is exact in fp64) and
+ * rounded once to fp32.  The routed experts' weighted sum plus the
+ * full-precision shared expert is the layer's output (dibi8.com ds4 guide,
+ * "Cac Doi Moi Kien Truc Chinh" item 1).  The steering term is runtime
+ * activation steering: a per-layer direction scaled by a strength chosen at
+ * run time, added to the FFN output without touching the weights
+ * (grapeot.me ds4 post, the activation-steering paragraphs on
+ * --dir-steering-ffn); the library adds it to the whole MoE layer output.
+ * shared_y: optional fp32 [T][H]; steer_dir: optional fp32 [H].
  * out_f32: fp32 [T][H] out; out_bf16: optional bf16 [T][H] copy (RNE). */
 int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
-                const float *topk_w, const float *shared_y, float *out_f32, uint16_t *out_bf16,
-                void *stream);
+                const float *topk_w, const float *shared_y, const float *steer_dir,
+                float steer_alpha, float *out_f32, uint16_t *out_bf16, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_forward: the whole layer, out = shared(x) + sum_j w_j FFN_{e_j}(x),
@@ -185,17 +255,16 @@ int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_po
  * host round trip).
  * logits_in / token_ids: as in moe_route.  out_f32: fp32 [T][H];
  * out_bf16, topk_idx_out [T][k], topk_w_out [T][k]: optional outputs.
- * Above one token the shared expert runs on a second stream that the library
- * creates once per host thread and device (default priority, no memory, kept
- * until the process ends), forked from `stream` by an event before any other
- * work and joined back before the combine, so the call still orders after
- * earlier work on `stream` and before later work, and can be captured into a
- * HIP graph from `stream`. */
+ * side: optional (NULL: everything on `stream`).  Above one token, when
+ * given, the shared expert runs on side->stream, forked from `stream` by
+ * side->fork before any other work and joined back by side->join before the
+ * combine, so the call still orders after earlier work on `stream` and
+ * before later work, and can be captured into a HIP graph from `stream`. */
 size_t moe_forward_workspace(const moe_layer *layer, int T);
 int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,
                 const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                 int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                void *stream);
+                const moe_side_stream *side, void *stream);
 
 /* moe_forward_marked: moe_forward for measurement tools.  Each kernel the
  * call enqueues (up to max_marks of them) is launched so that it records the
@@ -203,7 +272,9 @@ int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *l
  * void*) when it begins and ends on `stream` (HIP's extended launch), and
  * marks[i].name is set to a static string naming that kernel.  *n_marks gets
  * the number of kernels so timed.  Results are identical to moe_forward.
- * Every event must be non-null (MOE_EINVAL otherwise). */
+ * Every kernel runs on `stream` (no second stream), so that the timed
+ * kernels do not overlap.  Every event must be non-null (MOE_EINVAL
+ * otherwise). */
 typedef struct {
   void *start;
   void *stop;

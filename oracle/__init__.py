@@ -37,7 +37,8 @@ class Layer(C.Structure):
     _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("I_shared", C.c_int32), ("route_mode", C.c_int32),
                 ("w_router", C.c_void_p), ("gate", Proj), ("up", Proj), ("down", Proj),
-                ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p)]
+                ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+                ("steer_dir", C.c_void_p), ("steer_alpha", C.c_float)]
 
 
 _lib = None
@@ -72,7 +73,7 @@ def lib():
         L.orc_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_expert_ffn.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp]
         L.orc_shared_ffn.argtypes = [C.POINTER(Layer), i32, vp, vp]
-        L.orc_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.orc_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, C.c_float, vp]
         L.orc_forward.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp]
         L.orc_forward_a8.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp]
         L.orc_dense_masked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp]
@@ -80,6 +81,7 @@ def lib():
         L.orc_a8_swiglu_codes.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp]
         L.orc_a8_down.argtypes = [C.POINTER(Layer), vp, vp, vp, vp]
         L.orc_threads.restype = i32
+        L.orc_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -128,6 +130,11 @@ def threads():
     return int(lib().orc_threads())
 
 
+def set_threads(n):
+    """Threads of the oracle's parallel loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
 # --------------------------------------------------------------------------
 # weights
 # --------------------------------------------------------------------------
@@ -170,7 +177,7 @@ def dequant_matrix(p, expert=0):
 class LayerRef:
     """Binds a synth.Layer for the oracle calls."""
 
-    def __init__(self, layer, route_mode=0):
+    def __init__(self, layer, route_mode=0, steer_dir=None, steer_alpha=0.0):
         s = layer.spec
         self.layer = layer
         self.keep = []
@@ -184,9 +191,14 @@ class LayerRef:
                 a = _c(a, np.uint16)
                 self.keep.append(a)
                 sh.append(_p(a))
+        sd = None
+        if steer_dir is not None:
+            sd = _c(steer_dir, np.float32)
+            self.keep.append(sd)
         self.c = Layer(s.H, s.I, s.E, s.k, s.I_shared if layer.shared_gate is not None else 0,
                        route_mode, _p(wr), _proj(layer.gate, self.keep),
-                       _proj(layer.up, self.keep), _proj(layer.down, self.keep), *sh)
+                       _proj(layer.up, self.keep), _proj(layer.down, self.keep), *sh, _p(sd),
+                       float(steer_alpha))
         self.H, self.I, self.E, self.k = s.H, s.I, s.E, s.k
 
     def route(self, x, logits_in=None, token_ids=None, mode=None):
@@ -312,15 +324,16 @@ def dispatch(idx, E):
     return off, st, ss, sp
 
 
-def combine(y_rows, slot_pos, w, shared_y=None):
+def combine(y_rows, slot_pos, w, shared_y=None, steer_dir=None, steer_alpha=0.0):
     y = _c(y_rows, np.float32)
     sp = _c(slot_pos, np.int32)
     w = _c(w, np.float32)
     T, k = w.shape
     H = y.shape[1]
     sy = None if shared_y is None else _c(shared_y, np.float32)
+    sd = None if steer_dir is None else _c(steer_dir, np.float32)
     out = np.empty((T, H), np.float32)
-    lib().orc_combine(T, H, k, _p(y), _p(sp), _p(w), _p(sy), _p(out))
+    lib().orc_combine(T, H, k, _p(y), _p(sp), _p(w), _p(sy), _p(sd), float(steer_alpha), _p(out))
     return out
 
 

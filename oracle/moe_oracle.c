@@ -22,6 +22,16 @@ int orc_threads(void) {
 #endif
 }
 
+/* threads of the parallel loops from now on (n >= 1); the results do not
+ * depend on it */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* scalar decodes                                                             */
 /* ------------------------------------------------------------------------ */
@@ -550,16 +560,26 @@ int orc_shared_ffn(const orc_layer *L, int T, const uint16_t *x, float *y) {
   return rc;
 }
 
-/* out[t][n] = shared[t][n] + sum_j w[t][j] * y_rows[slot_pos[t*k + j]][n],
- * the sum taken in j order in fp64, stored as fp32 */
+/* Activation steering (grapeot.me ds4 post, the paragraphs on
+ * --dir-steering-ffn): at run time a per-layer direction, scaled by a chosen
+ * strength, is added to the FFN's output; the weights are untouched.
+ * Reading: it is added to the whole MoE layer output, after the routed sum. */
+static double steer_term(const float *dir, float alpha, int n) {
+  return dir ? (double)alpha * (double)dir[n] : 0.0;
+}
+
+/* out[t][n] = shared[t][n] + sum_j w[t][j] * y_rows[slot_pos[t*k + j]][n]
+ *             + alpha * dir[n],
+ * the sum taken in that order (j ascending) in fp64, stored as fp32 */
 void orc_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos, const float *w,
-                 const float *shared_y, float *out) {
+                 const float *shared_y, const float *steer_dir, float steer_alpha, float *out) {
   for (int t = 0; t < T; t++)
     for (int n = 0; n < H; n++) {
       double acc = shared_y ? (double)shared_y[(int64_t)t * H + n] : 0.0;
       for (int j = 0; j < k; j++)
         acc += (double)w[(int64_t)t * k + j] *
                (double)y_rows[(int64_t)slot_pos[(int64_t)t * k + j] * H + n];
+      if (steer_dir) acc += steer_term(steer_dir, steer_alpha, n);
       out[(int64_t)t * H + n] = (float)acc;
     }
 }
@@ -587,6 +607,7 @@ static int forward_impl(const orc_layer *L, int T, const uint16_t *x, const floa
         double acc = sh[(int64_t)t * H + h];
         for (int j = 0; j < k; j++)
           acc += (double)w[(int64_t)t * k + j] * y[(int64_t)sp[(int64_t)t * k + j] * H + h];
+        if (L->steer_dir) acc += steer_term(L->steer_dir, L->steer_alpha, h);
         out[(int64_t)t * H + h] = (float)acc;
       }
   free(off), free(st), free(ss), free(sp), free(y), free(sh);
@@ -630,7 +651,8 @@ int orc_dense_masked(const orc_layer *L, int T, const uint16_t *x, const int32_t
     free_expert(&ew);
   }
   if (rc == 0)
-    for (int64_t i = 0; i < (int64_t)T * H; i++) out[i] = (float)(sh[i] + acc[i]);
+    for (int64_t i = 0; i < (int64_t)T * H; i++)
+      out[i] = (float)(sh[i] + acc[i] + steer_term(L->steer_dir, L->steer_alpha, (int)(i % H)));
   free(sh), free(acc), free(xd), free(a), free(y);
   return rc;
 }

@@ -47,6 +47,8 @@ typedef struct {
   const uint16_t *w_router;    /* bf16 [E][H] */
   orc_proj gate, up, down;     /* [E][I][H], [E][I][H], [E][H][I] */
   const uint16_t *sh_gate, *sh_up, *sh_down; /* bf16 [Is][H], [Is][H], [H][Is]; NULL if none */
+  const float *steer_dir;      /* optional fp32 [H]: activation steering direction */
+  float steer_alpha;           /* its strength */
 } orc_layer;
 
 /* scalar decodes */
@@ -80,9 +82,11 @@ int orc_expert_ffn(const orc_layer *L, int T, const uint16_t *x, const int32_t *
                    const int32_t *sorted_token, float *y_rows);
 /* shared expert on all T tokens: y[t] = FFN_shared(x[t]) */
 int orc_shared_ffn(const orc_layer *L, int T, const uint16_t *x, float *y);
-/* combine: out[t] = shared[t] + sum_j w[t,j] * y_rows[slot_pos[t*k+j]] */
+/* combine: out[t] = shared[t] + sum_j w[t,j] * y_rows[slot_pos[t*k+j]]
+ *                  + steer_alpha * steer_dir (steer_dir optional) */
 void orc_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
-                 const float *w, const float *shared_y, float *out);
+                 const float *w, const float *shared_y, const float *steer_dir,
+                 float steer_alpha, float *out);
 
 /* whole layer (route -> dispatch -> expert FFN -> shared -> combine), fp64 inside */
 int orc_forward(const orc_layer *L, int T, const uint16_t *x, const float *logits_in,
@@ -109,6 +113,7 @@ int orc_a8_down(const orc_layer *L, const int32_t *offsets, const uint8_t *codes
                 const uint8_t *scales, float *y_rows);
 
 int orc_threads(void);
+void orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

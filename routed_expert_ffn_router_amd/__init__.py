@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 FMT_BF16, FMT_Q2K, FMT_VQ2, FMT_MXFP4 = 0, 1, 2, 3
 ROUTE_SOFTMAX_TOPK, ROUTE_HASH = 0, 1
 ACT_BF16, ACT_MXFP8 = 0, 1
+ACT_TRACE = 0x100  # with ACT_MXFP8 in expert_ffn: keep the fp32 SwiGLU output
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 
 
@@ -38,7 +39,12 @@ class Layer(C.Structure):
                 ("I_shared", C.c_int32), ("route_mode", C.c_int32), ("w_router", C.c_void_p),
                 ("gate", Weights), ("up", Weights), ("down", Weights),
                 ("shared_gate", C.c_void_p), ("shared_up", C.c_void_p),
-                ("shared_down", C.c_void_p), ("act_fmt", C.c_int32)]
+                ("shared_down", C.c_void_p), ("act_fmt", C.c_int32),
+                ("steer_dir", C.c_void_p), ("steer_alpha", C.c_float)]
+
+
+class SideStream(C.Structure):
+    _fields_ = [("stream", C.c_void_p), ("fork", C.c_void_p), ("join", C.c_void_p)]
 
 
 class Mark(C.Structure):
@@ -76,13 +82,20 @@ def lib():
         L.moe_expert_ffn.argtypes = [i32, i32, i32, vp, C.POINTER(Weights), C.POINTER(Weights),
                                      C.POINTER(Weights), i32, vp, vp, i32, vp, vp, sz, vp]
         L.moe_mxfp8_quantize.argtypes = [i32, i32, vp, vp, vp, vp]
-        L.moe_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, C.c_float, vp, vp, vp]
+        L.moe_expert_ffn_a8_layout.argtypes = [i32, i32, i32, i32, i32, C.POINTER(sz),
+                                               C.POINTER(sz), C.POINTER(sz)]
         L.moe_forward_workspace.restype = sz
         L.moe_forward_workspace.argtypes = [C.POINTER(Layer), i32]
-        L.moe_forward.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                  C.POINTER(SideStream), vp]
         L.moe_dequantize.argtypes = [C.POINTER(Weights), i32, i64, i64, vp, vp]
         L.moe_forward_marked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          C.POINTER(Mark), i32, C.POINTER(i32), vp]
+        L.moe_probe_read_blocks.restype = i32
+        L.moe_probe_read_blocks.argtypes = [sz]
+        L.moe_probe_hbm_read.argtypes = [vp, sz, vp, vp]
+        L.moe_probe_mfma.argtypes = [i32, i32, i32, vp, C.POINTER(C.c_double), vp]
         _lib = L
     return _lib
 
@@ -163,14 +176,17 @@ class DeviceLayer:
     """A whole MoE layer in device memory, with its moe_layer descriptor."""
 
     def __init__(self, H, I, E, k, route_mode, w_router, gate, up, down,
-                 shared_gate=None, shared_up=None, shared_down=None, act=ACT_BF16):
+                 shared_gate=None, shared_up=None, shared_down=None, act=ACT_BF16,
+                 steer_dir=None, steer_alpha=0.0):
         self.H, self.I, self.E, self.k, self.route_mode = H, I, E, k, route_mode
         self.act = act
         self.w_router, self.gate, self.up, self.down = w_router, gate, up, down
         self.shared_gate, self.shared_up, self.shared_down = shared_gate, shared_up, shared_down
+        self.steer_dir, self.steer_alpha = _dev(steer_dir, torch.float32, "steer_dir"), steer_alpha
         self.I_shared = 0 if shared_gate is None else shared_gate.shape[0]
         self.c = Layer(H, I, E, k, self.I_shared, route_mode, _ptr(w_router), gate.c, up.c, down.c,
-                       _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), act)
+                       _ptr(shared_gate), _ptr(shared_up), _ptr(shared_down), act,
+                       _ptr(steer_dir), float(steer_alpha))
 
     @classmethod
     def upload(cls, layer, route_mode=ROUTE_SOFTMAX_TOPK, device="cuda", act=ACT_BF16):
@@ -195,18 +211,25 @@ class DeviceLayer:
         return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, cl(self.w_router),
                            self.gate.clone(), self.up.clone(), self.down.clone(),
                            cl(self.shared_gate), cl(self.shared_up), cl(self.shared_down),
-                           self.act)
+                           self.act, cl(self.steer_dir), self.steer_alpha)
 
     def with_route_mode(self, mode):
         return DeviceLayer(self.H, self.I, self.E, self.k, mode, self.w_router, self.gate,
                            self.up, self.down, self.shared_gate, self.shared_up, self.shared_down,
-                           self.act)
+                           self.act, self.steer_dir, self.steer_alpha)
 
     def with_act(self, act):
         """The same weights with another activation format (MOE_ACT_*)."""
         return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, self.w_router,
                            self.gate, self.up, self.down, self.shared_gate, self.shared_up,
-                           self.shared_down, act)
+                           self.shared_down, act, self.steer_dir, self.steer_alpha)
+
+    def with_steering(self, steer_dir, steer_alpha):
+        """The same weights with an activation-steering direction (fp32 [H] on
+        the device, or None) and strength."""
+        return DeviceLayer(self.H, self.I, self.E, self.k, self.route_mode, self.w_router,
+                           self.gate, self.up, self.down, self.shared_gate, self.shared_up,
+                           self.shared_down, self.act, steer_dir, steer_alpha)
 
     def forward_workspace(self, T):
         return lib().moe_forward_workspace(C.byref(self.c), T)
@@ -256,8 +279,9 @@ def dispatch(topk_idx, E):
 
 
 def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows=None,
-               act=ACT_BF16):
-    """moe_expert_ffn -> y_rows fp32 [n_rows, H] (dense over x when offsets is None)."""
+               act=ACT_BF16, keep_ws=False):
+    """moe_expert_ffn -> y_rows fp32 [n_rows, H] (dense over x when offsets is None);
+    with keep_ws, (y_rows, workspace)."""
     _dev(x, BF16, "x")
     _dev(expert_offsets, torch.int32, "expert_offsets")
     _dev(sorted_token, torch.int32, "sorted_token")
@@ -271,7 +295,21 @@ def expert_ffn(x, gate, up, down, expert_offsets=None, sorted_token=None, n_rows
     _check(lib().moe_expert_ffn(T, H, I, _ptr(x), C.byref(gate.c), C.byref(up.c), C.byref(down.c),
                                 act, _ptr(expert_offsets), _ptr(sorted_token), n_rows, _ptr(y),
                                 _ptr(ws), ws.numel(), _stream()))
-    return y
+    return (y, ws) if keep_ws else y
+
+
+def a8_intermediate(ws, T, n_rows, E, H, I):
+    """The MX-FP8 SwiGLU output a MOE_ACT_MXFP8 moe_expert_ffn call left in its
+    workspace `ws`: (E4M3 codes uint8 [n_rows, I], E8M0 scales uint8 [n_rows, I/32],
+    fp32 values they were quantized from [n_rows, I] -- meaningful when the call
+    had ACT_TRACE)."""
+    co, so, fo = C.c_size_t(0), C.c_size_t(0), C.c_size_t(0)
+    _check(lib().moe_expert_ffn_a8_layout(T, n_rows, E, H, I, C.byref(co), C.byref(so),
+                                          C.byref(fo)))
+    codes = ws[co.value:co.value + n_rows * I].view(n_rows, I)
+    scales = ws[so.value:so.value + n_rows * (I // 32)].view(n_rows, I // 32)
+    vals = ws[fo.value:fo.value + 4 * n_rows * I].view(torch.float32).view(n_rows, I)
+    return codes, scales, vals
 
 
 def mxfp8_quantize(x):
@@ -284,31 +322,47 @@ def mxfp8_quantize(x):
     return q, sc
 
 
-def combine(y_rows, slot_pos, topk_w, shared_y=None, want_bf16=False):
+def combine(y_rows, slot_pos, topk_w, shared_y=None, want_bf16=False, steer_dir=None,
+            steer_alpha=0.0):
     """moe_combine -> (out fp32 [T, H], out bf16 bits [T, H] or None)."""
     _dev(y_rows, torch.float32, "y_rows")
     _dev(slot_pos, torch.int32, "slot_pos")
     _dev(topk_w, torch.float32, "topk_w")
     _dev(shared_y, torch.float32, "shared_y")
+    _dev(steer_dir, torch.float32, "steer_dir")
     T, k = topk_w.shape
     H = y_rows.shape[1]
     out = torch.empty((T, H), dtype=torch.float32, device=y_rows.device)
     ob = torch.empty((T, H), dtype=torch.int16, device=y_rows.device) if want_bf16 else None
     _check(lib().moe_combine(T, H, k, _ptr(y_rows), _ptr(slot_pos), _ptr(topk_w), _ptr(shared_y),
-                             _ptr(out), _ptr(ob), _stream()))
+                             _ptr(steer_dir), float(steer_alpha), _ptr(out), _ptr(ob),
+                             _stream()))
     return out, ob
 
 
 class Forward:
-    """moe_forward on a DeviceLayer with preallocated outputs and workspace."""
+    """moe_forward on a DeviceLayer with preallocated outputs and workspace.
 
-    def __init__(self, layer, T, device="cuda", want_bf16=False):
+    With side_stream (the default) it owns a second torch stream and two
+    events that moe_forward uses for the shared expert above one token."""
+
+    def __init__(self, layer, T, device="cuda", want_bf16=False, side_stream=True):
         self.layer, self.T = layer, T
         self.out = torch.empty((T, layer.H), dtype=torch.float32, device=device)
         self.out_bf16 = torch.empty((T, layer.H), dtype=torch.int16, device=device) if want_bf16 else None
         self.idx = torch.empty((T, layer.k), dtype=torch.int32, device=device)
         self.w = torch.empty((T, layer.k), dtype=torch.float32, device=device)
         self.ws = _ws(layer.forward_workspace(T), device)
+        self.side = None
+        if side_stream:
+            self._side_stream = torch.cuda.Stream(device=device)
+            self._fork = torch.cuda.Event()
+            self._join = torch.cuda.Event()
+            # torch creates the HIP events on first record
+            self._fork.record(self._side_stream)
+            self._join.record(self._side_stream)
+            self.side = SideStream(self._side_stream.cuda_stream, self._fork.cuda_event,
+                                   self._join.cuda_event)
 
     def __call__(self, x, logits_in=None, token_ids=None, layer=None):
         L = self.layer if layer is None else layer
@@ -317,7 +371,8 @@ class Forward:
         _dev(token_ids, torch.int64, "token_ids")
         _check(lib().moe_forward(C.byref(L.c), self.T, _ptr(x), _ptr(logits_in), _ptr(token_ids),
                                  _ptr(self.out), _ptr(self.out_bf16), _ptr(self.idx), _ptr(self.w),
-                                 _ptr(self.ws), self.ws.numel(), _stream()))
+                                 _ptr(self.ws), self.ws.numel(),
+                                 None if self.side is None else C.byref(self.side), _stream()))
         return self.out
 
 
@@ -349,3 +404,28 @@ def dequantize(proj, expert=0, w0=0, count=None):
     out = torch.empty(count, dtype=torch.float32, device=proj.data.device)
     _check(lib().moe_dequantize(C.byref(proj.c), expert, w0, count, _ptr(out), _stream()))
     return out
+
+
+# --------------------------------------------------------------------------
+# measurement probes (include/moe_probe.h)
+# --------------------------------------------------------------------------
+
+PROBE_BF16, PROBE_F16, PROBE_F8F4, PROBE_BF16_32, PROBE_F16_32 = 0, 1, 2, 3, 4
+
+
+def probe_sink_words(nbytes):
+    """uint32 words of sink that probe_hbm_read needs for an nbytes buffer."""
+    return int(lib().moe_probe_read_blocks(nbytes))
+
+
+def probe_hbm_read(buf, sink):
+    """moe_probe_hbm_read: stream-read the whole of `buf` (a GPU tensor)."""
+    _check(lib().moe_probe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                    _stream()))
+
+
+def probe_mfma(kind, blocks, iters, sink):
+    """moe_probe_mfma -> the flops the launch performs."""
+    fl = C.c_double(0.0)
+    _check(lib().moe_probe_mfma(kind, blocks, iters, _ptr(sink), C.byref(fl), _stream()))
+    return fl.value

@@ -28,6 +28,21 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+// the thread's error text, for the other translation units (probe.hip)
+int moe::set_error(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+namespace {
+
 int hip_check(hipError_t e, const char *where) {
   if (e == hipSuccess) return MOE_OK;
   return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
@@ -44,11 +59,12 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // Sequential carving of the caller's workspace (base == nullptr: sizing only).
 struct Carver {
   uint8_t *base;
-  size_t off = 0;
+  size_t off = 0, last = 0;  // last: offset of the latest piece
   explicit Carver(void *b) : base(static_cast<uint8_t *>(b)) {}
   template <class T>
   T *take(size_t n) {
     off = (off + 255) & ~size_t(255);
+    last = off;
     T *r = base ? reinterpret_cast<T *>(base + off) : nullptr;
     off += n * sizeof(T);
     return r;
@@ -132,38 +148,14 @@ struct Marker {
 
 void mark_cb(void *ctx, const char *name) { (*static_cast<Marker *>(ctx))(name); }
 
-// A second stream (default priority) with a fork and a join event, per host
-// thread and device: the shared expert does not depend on the routing, so
-// moe_forward runs it there, beside the router, the selection, the dispatch
-// and the routed FFN, and joins before the combine.  Per thread, so that one
-// thread's graph capture never takes in another thread's work.  Created on
-// first use and kept until the process ends; null (everything on the
-// caller's stream) if that fails.
+// The caller's second stream for the shared expert (moe_side_stream): it
+// does not depend on the routing, so moe_forward runs it there, beside the
+// router, the selection, the dispatch and the routed FFN, and joins before
+// the combine.
 struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t s;
+  hipEvent_t fork, join;
 };
-constexpr int kMaxDevices = 64;
-thread_local SideStream g_side[kMaxDevices];
-
-SideStream *side_stream() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream &ss = g_side[dev];
-  if (!ss.s) {
-    hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
-      if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(st);
-      return nullptr;
-    }
-    ss.s = st, ss.fork = f, ss.join = j;
-  }
-  return &ss;
-}
 
 WView bf16_view(const uint16_t *p, int N, int K) {
   return WView{MOE_FMT_BF16, 1, N, K, reinterpret_cast<const uint8_t *>(p), nullptr, nullptr};
@@ -193,7 +185,8 @@ FfnBufs carve_ffn(Carver &c, int T, int n_rows, int E, int H, int I, bool dense,
   b.a = c.take<float>((size_t)std::max(n_rows, 1) * I);
   b.tiles = c.take<int32_t>(gemm_tile_ints(std::max(n_rows, 1), dense ? 0 : E));
   b.x16 = c.take<uint16_t>((size_t)std::max(T, 1) * H);
-  if (act == MOE_ACT_MXFP8) b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, std::max(n_rows, 1)));
+  if ((act & ~MOE_ACT_TRACE) == MOE_ACT_MXFP8)
+    b.a8 = c.take<uint8_t>(a8_ws_bytes(T, H, I, std::max(n_rows, 1)));
   return b;
 }
 
@@ -217,9 +210,10 @@ int run_ffn(int T, int H, int I, const uint16_t *x, const WView &g, const WView 
             int n_rows, float *y, const FfnBufs &b, hipStream_t s, Marker *mk = nullptr) {
   Marker none;
   Marker &m = mk ? *mk : none;
-  if (act == MOE_ACT_MXFP8)
+  if ((act & ~MOE_ACT_TRACE) == MOE_ACT_MXFP8)
     return hip_check(launch_a8_ffn(g, u, d, H, I, T, x, offsets, sorted_token, n_rows, b.tiles,
-                                   b.a8, y, s, mark_cb, &m, kA8Names),
+                                   b.a8, (act & MOE_ACT_TRACE) ? b.a : nullptr, y, s, mark_cb,
+                                   &m, kA8Names),
                      "a8 ffn");
   if (!offsets && skinny_supported(H, I, T, g, d))
     return hip_check(launch_skinny_ffn(g, u, d, H, I, T, x, reinterpret_cast<uint16_t *>(b.a), y,
@@ -318,9 +312,10 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
 }
 
 int check_act(int act, int H, int I, const moe_weights *g, const moe_weights *u,
-              const moe_weights *d) {
+              const moe_weights *d, bool trace_ok = false) {
   if (act == MOE_ACT_BF16) return MOE_OK;
-  if (act != MOE_ACT_MXFP8) return fail(MOE_EINVAL, "unknown act_fmt %d", act);
+  if (act != MOE_ACT_MXFP8 && !(trace_ok && act == (MOE_ACT_MXFP8 | MOE_ACT_TRACE)))
+    return fail(MOE_EINVAL, "unknown act_fmt %d", act);
   if (!a8_supported(H, I, view_of(*g), view_of(*u), view_of(*d)))
     return fail(MOE_EUNSUPPORTED, "MX-FP8 activations need MXFP4 weights and H, I %% 512 == 0");
   return MOE_OK;
@@ -335,6 +330,8 @@ int check_layer(const moe_layer *L) {
   MOE_TRY(check_ffn_weights(L->E, L->H, L->I, &L->gate, &L->up, &L->down));
   MOE_TRY(check_act(L->act_fmt, L->H, L->I, &L->gate, &L->up, &L->down));
   if (L->I_shared < 0) return fail(MOE_EINVAL, "I_shared < 0");
+  if (L->steer_dir && !aligned(L->steer_dir, 16))
+    return fail(MOE_EINVAL, "steer_dir misaligned");
   if (L->I_shared > 0 && L->shared_gate) {
     if (!L->shared_up || !L->shared_down) return fail(MOE_EINVAL, "incomplete shared expert");
     if (!aligned(L->shared_gate, 16) || !aligned(L->shared_up, 16) ||
@@ -430,6 +427,27 @@ size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_
   return c.size();
 }
 
+int moe_expert_ffn_a8_layout(int T, int n_rows, int E, int H, int I, size_t *codes_off,
+                             size_t *scales_off, size_t *f32_off) {
+  if (T < 1 || n_rows < 1 || E < 1 || I < 32 || H < 1 || I % 32)
+    return fail(MOE_EINVAL, "bad sizes T = %d, n_rows = %d, E = %d, H = %d, I = %d", T, n_rows,
+                E, H, I);
+  if (!codes_off || !scales_off || !f32_off) return fail(MOE_EINVAL, "null output");
+  Carver c(nullptr);
+  FfnBufs b = carve_ffn(c, T, n_rows, E, H, I, false, MOE_ACT_MXFP8);
+  (void)b;
+  const size_t a8 = c.last;  // the MX-FP8 region is carved last
+  {
+    Carver d(reinterpret_cast<void *>(uintptr_t(256)));  // offsets relative to a fake base
+    *f32_off = reinterpret_cast<uintptr_t>(
+                   carve_ffn(d, T, n_rows, E, H, I, false, MOE_ACT_MXFP8).a) - 256;
+  }
+  a8_layout(T, H, I, n_rows, codes_off, scales_off);
+  *codes_off += a8;
+  *scales_off += a8;
+  return MOE_OK;
+}
+
 int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *gate,
                    const moe_weights *up, const moe_weights *down, int act_fmt,
                    const int32_t *expert_offsets, const int32_t *sorted_token, int n_rows,
@@ -438,7 +456,7 @@ int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *ga
   if (!gate) return fail(MOE_EINVAL, "null gate");
   const int E = gate->n_experts;
   MOE_TRY(check_ffn_weights(E, H, I, gate, up, down));
-  MOE_TRY(check_act(act_fmt, H, I, gate, up, down));
+  MOE_TRY(check_act(act_fmt, H, I, gate, up, down, true));
   if (T == 0 || n_rows == 0) return MOE_OK;
   if (!x || !y_rows) return fail(MOE_EINVAL, "null x or y_rows");
   if (!aligned(x, 16) || !aligned(y_rows, 16)) return fail(MOE_EINVAL, "x/y_rows misaligned");
@@ -456,17 +474,17 @@ int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *ga
 }
 
 int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
-                const float *topk_w, const float *shared_y, float *out_f32, uint16_t *out_bf16,
-                void *stream) {
+                const float *topk_w, const float *shared_y, const float *steer_dir,
+                float steer_alpha, float *out_f32, uint16_t *out_bf16, void *stream) {
   if (T < 0 || H < 1 || k < 1 || k > 16) return fail(MOE_EINVAL, "bad T/H/k");
   if (T == 0) return MOE_OK;
   if (H % 4) return fail(MOE_EINVAL, "H = %d must be a multiple of 4", H);
   if (!y_rows || !slot_pos || !topk_w || !out_f32) return fail(MOE_EINVAL, "null combine pointer");
   if (!aligned(y_rows, 16) || !aligned(out_f32, 16) || (shared_y && !aligned(shared_y, 16)) ||
-      (out_bf16 && !aligned(out_bf16, 8)))
+      (steer_dir && !aligned(steer_dir, 16)) || (out_bf16 && !aligned(out_bf16, 8)))
     return fail(MOE_EINVAL, "combine buffers misaligned");
-  return hip_check(launch_combine(T, H, k, y_rows, slot_pos, topk_w, shared_y, out_f32, out_bf16,
-                                  as_stream(stream)),
+  return hip_check(launch_combine(T, H, k, y_rows, slot_pos, topk_w, shared_y, steer_dir,
+                                  steer_alpha, out_f32, out_bf16, as_stream(stream)),
                    "combine");
 }
 
@@ -480,7 +498,7 @@ size_t moe_forward_workspace(const moe_layer *L, int T) {
 static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
                         const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                         int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                        void *stream, Marker &mk) {
+                        const moe_side_stream *side_in, void *stream, Marker &mk) {
   MOE_TRY(check_layer(L));
   if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
   if (T == 0) return MOE_OK;
@@ -489,6 +507,10 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     return fail(MOE_EINVAL, "x/out misaligned");
   if (L->route_mode == MOE_ROUTE_HASH && !token_ids)
     return fail(MOE_EINVAL, "hash routing needs token_ids");
+  if (side_in && (!side_in->stream || !side_in->fork || !side_in->join))
+    return fail(MOE_EINVAL, "side stream: stream, fork and join must all be given");
+  if (side_in && side_in->stream == stream)
+    return fail(MOE_EINVAL, "side stream: must differ from the call's stream");
   const size_t need = moe_forward_workspace(L, T);
   if (!ws || ws_bytes < need)
     return fail(MOE_ENOSPC, "forward workspace: %zu bytes < %zu", ws_bytes, need);
@@ -517,12 +539,20 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     a.a_hi = reinterpret_cast<uint16_t *>(b.a);
     a.a_lo = a.a_hi + (size_t)k * I;
     a.topk_idx = idx, a.topk_w = w, a.out = out_f32, a.out_bf16 = out_bf16;
+    a.steer_dir = L->steer_dir, a.steer_alpha = L->steer_alpha;
     return hip_check(launch_decode1(a, s, mark_cb, &mk), "decode");
   }
   const bool shared = L->I_shared > 0 && L->shared_gate;
-  // the shared expert goes first, on the side stream where one exists (not
-  // when each kernel is timed: the marks time one stream)
-  SideStream *side = shared && !mk.m ? side_stream() : nullptr;
+  // the shared expert goes first, on the caller's side stream when one is
+  // given (not when each kernel is timed: the marks time one stream)
+  SideStream side_v{};
+  SideStream *side = nullptr;
+  if (shared && !mk.m && side_in) {
+    side_v.s = as_stream(side_in->stream);
+    side_v.fork = static_cast<hipEvent_t>(side_in->fork);
+    side_v.join = static_cast<hipEvent_t>(side_in->join);
+    side = &side_v;
+  }
   if (side) {
     MOE_TRY(hip_check(hipEventRecord(side->fork, s), "fork"));
     MOE_TRY(hip_check(hipStreamWaitEvent(side->s, side->fork, 0), "fork"));
@@ -581,7 +611,7 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
                         "select"));
       if (L->act_fmt == MOE_ACT_MXFP8)
         return hip_check(launch_a8_ffn(g, u, d, H, I, T, x, b.offsets, b.sorted_token, n, b.tiles,
-                                       b.a8, b.y_rows, s, mark_cb, &mk, kA8Names),
+                                       b.a8, nullptr, b.y_rows, s, mark_cb, &mk, kA8Names),
                          "a8 ffn");
       if (use_gemm(T, H, I, E, n, false, g.fmt, d.fmt))
         // several tokens: every selected expert's weights once, all its rows per load
@@ -612,18 +642,18 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
   if (rc != MOE_OK) return rc;
   if (rc_join != MOE_OK) return rc_join;
   mk("combine");
-  return hip_check(
-      launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, out_f32, out_bf16, s),
-      "combine");
+  return hip_check(launch_combine(T, H, k, b.y_rows, b.slot_pos, w, b.shared_y, L->steer_dir,
+                                  L->steer_alpha, out_f32, out_bf16, s),
+                   "combine");
 }
 
 int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
                 const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                 int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                void *stream) {
+                const moe_side_stream *side, void *stream) {
   Marker none;
   return forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out, topk_w_out,
-                      ws, ws_bytes, stream, none);
+                      ws, ws_bytes, side, stream, none);
 }
 
 int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
@@ -637,7 +667,7 @@ int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float
   mk.m = marks;
   mk.max = max_marks;
   const int rc = forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out,
-                              topk_w_out, ws, ws_bytes, stream, mk);
+                              topk_w_out, ws, ws_bytes, nullptr, stream, mk);
   if (n_marks) *n_marks = mk.n;
   return rc;
 }

@@ -179,7 +179,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   // each wave goes on as soon as the selection and the codebook are written,
   // without waiting for the other waves' shared rows (a bounded wait on an
-  // LDS counter that waves of this block always complete)
+  // LDS counter that waves of this block always complete; were the bound
+  // ever reached, the expert index is still clamped into [0, E), so every
+  // load stays inside the weights)
   {
     const int need = RFMT == MOE_FMT_VQ2 ? 5 : 1;
     for (int it = 0; it < (1 << 22); it++) {
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int ST = steps_for<RFMT, RSPL>();
   const int j = blockIdx.x / p.tiles_per_expert, tile = blockIdx.x % p.tiles_per_expert;
   const int row_base = (tile * kDecWaves + wave) * ST;
-  const int e_sel = __builtin_amdgcn_readfirstlane(s_e[j]);
+  const int e_sel = min(max(__builtin_amdgcn_readfirstlane(s_e[j]), 0), p.E - 1);
   // every routed row pair's loads go out at once (MXFP4's larger chunks: two)
   constexpr int kRPF = RFMT == MOE_FMT_MXFP4 ? 2 : ST;
   gateup_rows<RFMT, RSPL, 64, ST, 1, kRPF, kCopies>(p.gate, p.up, p.H, p.I, p.x, e_sel, j, j + 1,
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
 #pragma unroll
       for (int w = 0; w < kDecWaves; w++) v += s_part[w][r];
       if (p.Is) v += p.shared_y[row];
+      if (p.steer_dir) v = fmaf(p.steer_alpha, p.steer_dir[row], v);
       p.out[row] = v;
       if (p.out_bf16) p.out_bf16[row] = (uint16_t)f32_to_bf16_bits(v);
     }

@@ -114,6 +114,7 @@ struct A8Args {
   const int32_t *tiles;
   int weight_major;
   uint8_t *out_q, *out_s;  // gate/up: MX-FP8 SwiGLU output [n_rows][N], [n_rows][N / 32]
+  float *a_f32;            // gate/up, optional: the SwiGLU output before quantization [n_rows][N]
   float *y_out;            // down: fp32 [n_rows][N]
 };
 
@@ -301,6 +302,10 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
           for (int c = 0; c < 2; c++)
             p.out_q[base + 16 * c + lr] =
                 (uint8_t)(amax > 0.0f ? e4m3_code(__builtin_ldexpf(a[c], sh)) : 0u);
+          if (p.a_f32) {
+#pragma unroll
+            for (int c = 0; c < 2; c++) p.a_f32[base + 16 * c + lr] = a[c];
+          }
           if (lr == 0) p.out_s[(size_t)r * (p.N / 32) + (n0 + kWaveCols * wave) / 32] = (uint8_t)e8;
         }
       } else {
@@ -329,13 +334,19 @@ size_t a8_ws_bytes(int T, int H, int I, int n_rows) {
          up((size_t)n_rows * I / 32);
 }
 
+void a8_layout(int T, int H, int I, int n_rows, size_t *codes_off, size_t *scales_off) {
+  auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+  *codes_off = up((size_t)T * H) + up((size_t)T * H / 32);
+  *scales_off = *codes_off + up((size_t)n_rows * I);
+}
+
 namespace {
 
 template <int BM>
 hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, int I, int T,
                  const int32_t *offsets, const int32_t *sorted_token, int n_rows, int32_t *tiles,
-                 const uint8_t *xq, const uint8_t *xs, uint8_t *aq, uint8_t *as, float *y,
-                 hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
+                 const uint8_t *xq, const uint8_t *xs, uint8_t *aq, uint8_t *as, float *a_trace,
+                 float *y, hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
                  const char *const names[3]) {
   const int E = offsets ? gate.E : 0;
   // tiles: sum over the active experts of ceil(rows / BM) <= n_rows / BM + the
@@ -349,7 +360,7 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   A8Args g{};
   g.K = H, g.N = I, g.w0 = gate, g.w1 = up, g.aq = xq, g.as = xs, g.a_rows = T;
   g.row_token = offsets ? sorted_token : nullptr;
-  g.tiles = tiles, g.out_q = aq, g.out_s = as;
+  g.tiles = tiles, g.out_q = aq, g.out_s = as, g.a_f32 = a_trace;
   g.weight_major = !offsets && (I / a8_block_cols<kModeGateUp>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
   err = launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
@@ -370,17 +381,20 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
 hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                          int T, const uint16_t *x, const int32_t *offsets,
                          const int32_t *sorted_token, int n_rows, int32_t *tiles, void *ws,
-                         float *y, hipStream_t s, void (*mark)(void *, const char *),
-                         void *mark_ctx, const char *const names[4]) {
+                         float *a_trace, float *y, hipStream_t s,
+                         void (*mark)(void *, const char *), void *mark_ctx,
+                         const char *const names[4]) {
   if (!a8_supported(H, I, gate, up, down) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
   if ((size_t)T * H >= ((size_t)1 << 31) || (size_t)n_rows * I >= ((size_t)1 << 31))
     return hipErrorInvalidValue;
   auto up256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+  size_t codes_off, scales_off;
+  a8_layout(T, H, I, n_rows, &codes_off, &scales_off);
   uint8_t *w = static_cast<uint8_t *>(ws);
   uint8_t *xq = w;
   uint8_t *xs = xq + up256((size_t)T * H);
-  uint8_t *aq = xs + up256((size_t)T * H / 32);
-  uint8_t *as = aq + up256((size_t)n_rows * I);
+  uint8_t *aq = w + codes_off;
+  uint8_t *as = w + scales_off;
   if (mark) mark(mark_ctx, names[3]);
   const long n8 = (long)T * (H / 8);
   hipError_t err =
@@ -389,9 +403,9 @@ hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, 
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
   if (n_rows >= 32 * active)
     return a8_bm<64>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq,
-                     as, y, s, mark, mark_ctx, names);
+                     as, a_trace, y, s, mark, mark_ctx, names);
   return a8_bm<16>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq, as,
-                   y, s, mark, mark_ctx, names);
+                   a_trace, y, s, mark, mark_ctx, names);
 }
 
 // MX-FP8 quantization alone (for tests of the quantizer)

@@ -16,6 +16,8 @@ namespace moe {
 // its own start and end (HIP's extended launch); an unarmed launch records
 // nothing.  The arming is per host thread and consumed by that launch.
 void timer_arm(hipEvent_t start, hipEvent_t stop);
+// sets the calling thread's moe_last_error() text; returns code
+int set_error(int code, const char *fmt, ...);
 void timer_take(hipEvent_t *start, hipEvent_t *stop);
 
 template <typename... P, size_t... I>
@@ -132,14 +134,19 @@ hipError_t launch_tile_list(int E, int n_dense, int bm, const int32_t *offsets, 
 
 // MXFP4 experts with MX-FP8 activations on the FP4 matrix instructions
 // (gemm_fp4.hip): ws of a8_ws_bytes(T, H, I, n_rows) holds the quantized
-// tokens and SwiGLU output; names: tile list, gate/up, down, quantization
+// tokens and SwiGLU output; a_trace (optional, fp32 [n_rows][I]) gets the
+// SwiGLU output before its quantization; names: tile list, gate/up, down,
+// quantization
 bool a8_supported(int H, int I, const WView &gate, const WView &up, const WView &down);
 size_t a8_ws_bytes(int T, int H, int I, int n_rows);
+// byte offsets, inside that region, of the SwiGLU output's E4M3 codes and scales
+void a8_layout(int T, int H, int I, int n_rows, size_t *codes_off, size_t *scales_off);
 hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, int H, int I,
                          int T, const uint16_t *x, const int32_t *offsets,
                          const int32_t *sorted_token, int n_rows, int32_t *tiles, void *ws,
-                         float *y, hipStream_t s, void (*mark)(void *, const char *),
-                         void *mark_ctx, const char *const names[4]);
+                         float *a_trace, float *y, hipStream_t s,
+                         void (*mark)(void *, const char *), void *mark_ctx,
+                         const char *const names[4]);
 hipError_t launch_mx8_quant(int rows, int K, const uint16_t *x, uint8_t *q, uint8_t *sc,
                             hipStream_t s);
 
@@ -171,6 +178,8 @@ struct DecodeArgs {
   float *shared_y;           // [H] shared expert output (written by p2)
   float *out;                // [H]
   uint16_t *out_bf16;        // optional [H]
+  const float *steer_dir;    // optional [H]: out += steer_alpha * steer_dir
+  float steer_alpha;
   int nb_router, nb_shared_gu, nb_routed, tiles_per_expert;
 };
 
@@ -180,7 +189,7 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
 
 // combine -----------------------------------------------------------------
 hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,
-                          const float *w, const float *shared_y, float *out, uint16_t *out_bf16,
-                          hipStream_t s);
+                          const float *w, const float *shared_y, const float *steer_dir,
+                          float steer_alpha, float *out, uint16_t *out_bf16, hipStream_t s);
 
 }  // namespace moe

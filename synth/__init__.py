@@ -81,6 +81,14 @@ WORKLOADS = {
         Workload("tiny_t4", TINY, 4),
         Workload("decode_b1", Q2, 1),
         Workload("decode_b16_zipf", Q2, 16, logits="zipf"),
+        # speculative-decode verification: each session checks its next token
+        # plus 5 drafted ones in one step (1 + 5 = 6 tokens); one session, or
+        # 16 sessions batched (96 tokens).  Tokens are drawn independently:
+        # consecutive positions of one sequence would share experts more often.
+        Workload("verify_t6", Q2, 6),
+        Workload("verify_t6_zipf", Q2, 6, logits="zipf"),
+        Workload("verify_t96", Q2, 96),
+        Workload("verify_t96_zipf", Q2, 96, logits="zipf"),
         Workload("prefill_2048", Q2, 2048),
         Workload("prefill_4096", Q2, 4096),
         Workload("mxfp4_decode_b1", MX, 1),

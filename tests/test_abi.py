@@ -2,6 +2,7 @@
 include/moe.h declares, and rejects bad arguments on the host before any HIP
 call (so these run in a container with no GPU)."""
 import ctypes as C
+import glob
 import os
 import re
 
@@ -20,9 +21,12 @@ def _lib():
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+    """Every function declared by the headers under include/."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -30,7 +34,8 @@ def test_header_declares_the_boundary():
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
               "moe_dequantize", "moe_last_error", "moe_abi_version", "moe_route_workspace",
               "moe_dispatch_workspace", "moe_expert_ffn_workspace", "moe_forward_workspace",
-              "moe_mxfp8_quantize"]:
+              "moe_mxfp8_quantize", "moe_expert_ffn_a8_layout", "moe_probe_hbm_read",
+              "moe_probe_mfma", "moe_probe_read_blocks"]:
         assert n in names
 
 
@@ -41,7 +46,19 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
+
+
+def test_library_creates_no_hip_objects():
+    """No stream, event, graph or memory of the library's own: every HIP
+    object it touches is the caller's."""
+    csrc = os.path.join(ROOT, "routed_expert_ffn_router_amd", "csrc")
+    banned = re.compile(r"\b(hip(Stream|Event|Graph)Create\w*|hipMalloc\w*|hipFree\w*|"
+                        r"hipHostMalloc|thread_local\s+\w*Stream)")
+    for f in sorted(os.listdir(csrc)):
+        src = open(os.path.join(csrc, f)).read()
+        src = re.sub(r"//[^\n]*", "", src)
+        assert not banned.search(src), (f, banned.search(src).group(0))
 
 
 def _w(fmt=moe.FMT_VQ2, E=8, N=2048, K=4096, data=FAKE, scales=FAKE, cb=FAKE):
@@ -134,10 +151,13 @@ def test_expert_ffn_rejects_bad_arguments():
 
 def test_combine_and_dequantize_reject_bad_arguments():
     lib = _lib()
-    assert lib.moe_combine(4, 4096, 0, FAKE, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
-    assert lib.moe_combine(4, 4094, 8, FAKE, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
-    assert lib.moe_combine(4, 4096, 8, None, FAKE, FAKE, None, FAKE, None, None) == moe.EINVAL
-    assert lib.moe_combine(0, 4096, 8, None, None, None, None, None, None, None) == moe.OK
+    c = lib.moe_combine
+    assert c(4, 4096, 0, FAKE, FAKE, FAKE, None, None, 0.0, FAKE, None, None) == moe.EINVAL
+    assert c(4, 4094, 8, FAKE, FAKE, FAKE, None, None, 0.0, FAKE, None, None) == moe.EINVAL
+    assert c(4, 4096, 8, None, FAKE, FAKE, None, None, 0.0, FAKE, None, None) == moe.EINVAL
+    assert c(4, 4096, 8, FAKE, FAKE, FAKE, None, FAKE + 4, 1.0, FAKE, None, None) == moe.EINVAL
+    assert "misaligned" in _err()
+    assert c(0, 4096, 8, None, None, None, None, None, 0.0, None, None, None) == moe.OK
     w = _w(moe.FMT_Q2K, 2, 64, 256, FAKE, None, None)
     dq = lib.moe_dequantize
     assert dq(C.byref(w), 2, 0, 10, FAKE, None) == moe.EINVAL
@@ -157,12 +177,51 @@ def test_forward_validation_and_workspace_sizes():
     ws2048 = lib.moe_forward_workspace(C.byref(L), 2048)
     assert 0 < ws1 < ws2048
     f = lib.moe_forward
-    assert f(C.byref(L), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1 - 1, None) == moe.ENOSPC
-    assert f(C.byref(L), 0, None, None, None, None, None, None, None, None, 0, None) == moe.OK
+
+    def call(L=L, T=1, ws=ws1, side=None):
+        return f(C.byref(L), T, FAKE, None, None, FAKE, None, None, None, FAKE, ws,
+                 None if side is None else C.byref(side), FAKE + 256)
+
+    assert call(ws=ws1 - 1) == moe.ENOSPC
+    assert f(C.byref(L), 0, None, None, None, None, None, None, None, None, 0, None, None) == moe.OK
     Lh = moe.Layer(4096, 2048, 256, 8, 2048, 1, FAKE, g, u, d, FAKE, FAKE, FAKE)
-    assert f(C.byref(Lh), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1, None) == moe.EINVAL
+    assert call(Lh) == moe.EINVAL
     Lk = moe.Layer(4096, 2048, 256, 0, 2048, 0, FAKE, g, u, d, FAKE, FAKE, FAKE)
-    assert f(C.byref(Lk), 1, FAKE, None, None, FAKE, None, None, None, FAKE, ws1, None) == moe.EINVAL
+    assert call(Lk) == moe.EINVAL
+    # the caller's second stream: all three handles, and not the call's own stream
+    assert call(side=moe.SideStream(FAKE, FAKE, None)) == moe.EINVAL and "side" in _err()
+    assert call(side=moe.SideStream(FAKE + 256, FAKE, FAKE)) == moe.EINVAL
+    # the fp32 trace is for moe_expert_ffn only
+    mg = _w(moe.FMT_MXFP4, 256, 2048, 4096, FAKE, FAKE, None)
+    md = _w(moe.FMT_MXFP4, 256, 4096, 2048, FAKE, FAKE, None)
+    La = moe.Layer(4096, 2048, 256, 8, 2048, 0, FAKE, mg, mg, md, FAKE, FAKE, FAKE,
+                   moe.ACT_MXFP8 | moe.ACT_TRACE, None, 0.0)
+    assert call(La, ws=lib.moe_forward_workspace(C.byref(La), 1)) == moe.EINVAL
+        # a steering direction must be 16-byte aligned
+    Ls = moe.Layer(4096, 2048, 256, 8, 2048, 0, FAKE, g, u, d, FAKE, FAKE, FAKE, 0, FAKE + 8, 1.0)
+    assert call(Ls) == moe.EINVAL and "steer" in _err()
+
+
+def test_a8_layout_inside_the_workspace():
+    lib = _lib()
+    for T, n, E, H, I in [(1, 8, 256, 4096, 2048), (4096, 32768, 256, 4096, 2048),
+                          (3, 6, 8, 512, 512)]:
+        co, so, fo = C.c_size_t(0), C.c_size_t(0), C.c_size_t(0)
+        assert lib.moe_expert_ffn_a8_layout(T, n, E, H, I, C.byref(co), C.byref(so),
+                                            C.byref(fo)) == moe.OK
+        ws = lib.moe_expert_ffn_workspace(T, n, E, H, I, moe.FMT_MXFP4, moe.FMT_MXFP4,
+                                          moe.ACT_MXFP8)
+        assert ws == lib.moe_expert_ffn_workspace(T, n, E, H, I, moe.FMT_MXFP4, moe.FMT_MXFP4,
+                                                  moe.ACT_MXFP8 | moe.ACT_TRACE)
+        assert co.value % 256 == 0 and so.value % 256 == 0 and fo.value % 256 == 0
+        assert co.value + n * I <= so.value and so.value + n * I // 32 <= ws
+        # the fp32 trace lies before the MX-FP8 region, clear of it
+        assert fo.value + 4 * n * I <= co.value
+    co = C.c_size_t(0)
+    assert lib.moe_expert_ffn_a8_layout(1, 8, 8, 512, 100, C.byref(co), C.byref(co),
+                                        C.byref(co)) == moe.EINVAL
+    assert lib.moe_expert_ffn_a8_layout(1, 8, 8, 512, 512, None, C.byref(co),
+                                        C.byref(co)) == moe.EINVAL
 
 
 def test_binding_refuses_host_tensors():
