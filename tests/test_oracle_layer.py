@@ -312,3 +312,57 @@ def test_a8_stages_compose_to_forward():
     assert _normwise(ref, out.astype(np.float64)) < 1e-6
     # and differs from the plain layer's rows by the MX-FP8 effect
     assert _normwise(y, R.expert_ffn(x, off, st).astype(np.float64)) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# activation steering: out += alpha * dir, added after the routed sum
+# --------------------------------------------------------------------------
+
+def _unit_dir(H, seed):
+    d = np.random.default_rng(seed).standard_normal(H)
+    return (d / np.linalg.norm(d)).astype(np.float32)
+
+
+def test_steering_alone_is_alpha_dir():
+    """With every routed weight zero and no shared expert the layer's output
+    is the steering term alone: fp32(alpha * dir), one rounding of the exact
+    product."""
+    spec = _spec(Is=0)
+    L = synth.gen_layer(spec, 5)
+    L.down.data[:] = 0
+    d = _unit_dir(256, 6)
+    for alpha in (2.0, -1.0, 0.3):
+        out, _, _ = oracle.LayerRef(L, steer_dir=d, steer_alpha=alpha).forward(synth.gen_x(256, 3, 7))
+        want = (np.float64(np.float32(alpha)) * d.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(out, np.tile(want, (3, 1)))
+
+
+def test_steering_shifts_the_layer_by_alpha_dir():
+    """Steered minus plain output is alpha * dir, within the fp32 rounding of
+    the two outputs; strength 0 changes nothing."""
+    L = synth.gen_layer(synth.TINY, 8)
+    x = synth.gen_x(256, 5, 9)
+    d = _unit_dir(256, 10)
+    plain, idx, w = oracle.LayerRef(L).forward(x)
+    for alpha in (2.0, -1.0):
+        out, idx2, w2 = oracle.LayerRef(L, steer_dir=d, steer_alpha=alpha).forward(x)
+        assert np.array_equal(idx, idx2) and np.array_equal(w, w2)
+        delta = out.astype(np.float64) - plain - alpha * d.astype(np.float64)
+        assert np.abs(delta).max() <= 2 * 2.0 ** -24 * np.abs(out).max()
+    zero, _, _ = oracle.LayerRef(L, steer_dir=d, steer_alpha=0.0).forward(x)
+    assert np.array_equal(zero, plain)
+
+
+def test_steering_dense_masked_equals_bucketed():
+    L = synth.gen_layer(synth.TINY, 11)
+    x = synth.gen_x(256, 6, 12)
+    d = _unit_dir(256, 13)
+    R = oracle.LayerRef(L, steer_dir=d, steer_alpha=-1.5)
+    out, idx, w = R.forward(x)
+    dense = R.dense_masked(x, idx, w)
+    np.testing.assert_allclose(out, dense, rtol=0, atol=1e-6 * np.abs(dense).max())
+    # and the steered combine of the bucketed pieces
+    off, st, _, sp = oracle.dispatch(idx, L.spec.E)
+    y = R.expert_ffn(x, off, st)
+    ref = oracle.combine(y, sp, w, R.shared_ffn(x), d, -1.5)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
