@@ -26,8 +26,9 @@
  *    reported by these calls.
  *  - T == 0 (no tokens) is a valid no-op.
  *  - Calls are reentrant; concurrent calls must use distinct ws buffers.
- *    The library holds no mutable state of its own and creates no HIP
- *    objects: every stream and event it uses is the caller's.
+ *    The library creates no HIP objects -- every stream and event it uses is
+ *    the caller's -- and holds no mutable state of its own, except the
+ *    device scratch of moe_forward_static (below).
  *
  * Value ranges (preconditions the host cannot check without reading device
  * memory; outside them results may be inf/NaN where the CPU reference is
@@ -265,6 +266,22 @@ int moe_forward(const moe_layer *layer, int T, const uint16_t *x, const float *l
                 const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                 int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                 const moe_side_stream *side, void *stream);
+
+/* moe_forward_static: moe_forward for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no ws argument and no allocation of any kind; the workspace
+ * is a device array of MOE_STATIC_SCRATCH_BYTES inside the library, one per
+ * GPU, held from the first call on that GPU until the process ends.  Layers
+ * and token counts whose moe_forward_workspace exceeds it return
+ * MOE_ENOSPC (64 MiB: up to 256 tokens of a 4096-hidden, 256-expert top-8
+ * layer).  Everything runs on `stream` (no second stream).  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Results are identical to moe_forward's. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_static(const moe_layer *layer, int T, const uint16_t *x, const float *logits_in,
+                       const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                       int32_t *topk_idx_out, float *topk_w_out, void *stream);
 
 /* moe_forward_marked: moe_forward for measurement tools.  Each kernel the
  * call enqueues (up to max_marks of them) is launched so that it records the

@@ -92,6 +92,7 @@ def lib():
         L.moe_dequantize.argtypes = [C.POINTER(Weights), i32, i64, i64, vp, vp]
         L.moe_forward_marked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          C.POINTER(Mark), i32, C.POINTER(i32), vp]
+        L.moe_forward_static.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_probe_read_blocks.restype = i32
         L.moe_probe_read_blocks.argtypes = [sz]
         L.moe_probe_hbm_read.argtypes = [vp, sz, vp, vp]
@@ -388,6 +389,18 @@ class Forward:
                                         _ptr(self.idx), _ptr(self.w), _ptr(self.ws), self.ws.numel(),
                                         marks, len(events), C.byref(n), _stream()))
         return [marks[i].name.decode() for i in range(n.value)]
+
+
+def forward_static(layer, x, out, idx, w, logits_in=None, token_ids=None, out_bf16=None):
+    """moe_forward_static into preallocated outputs (out fp32 [T, H], idx int32
+    [T, k], w fp32 [T, k]): no workspace, no allocation."""
+    _dev(x, BF16, "x")
+    _dev(logits_in, torch.float32, "logits_in")
+    _dev(token_ids, torch.int64, "token_ids")
+    _check(lib().moe_forward_static(C.byref(layer.c), x.shape[0], _ptr(x), _ptr(logits_in),
+                                    _ptr(token_ids), _ptr(out), _ptr(out_bf16), _ptr(idx),
+                                    _ptr(w), _stream()))
+    return out
 
 
 def forward(layer, x, logits_in=None, token_ids=None):

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -654,6 +655,56 @@ int moe_forward(const moe_layer *L, int T, const uint16_t *x, const float *logit
   Marker none;
   return forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out, topk_w_out,
                       ws, ws_bytes, side, stream, none);
+}
+
+// ---------------------------------------------------------------------------
+// moe_forward_static: moe_forward on a scratch buffer the library owns, for
+// callers that cannot allocate.  The buffer is a file-scope device array; in
+// host code its name is only a stand-in, so its address on each device is
+// taken once with hipGetSymbolAddress (with that device current) and kept.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+int static_scratch(void **out) {
+  int dev = -1;
+  MOE_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MOE_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    MOE_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress"));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_forward_static(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
+                       const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
+                       int32_t *topk_idx_out, float *topk_w_out, void *stream) {
+  MOE_TRY(check_layer(L));
+  if (T < 0) return fail(MOE_EINVAL, "T = %d < 0", T);
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_forward_workspace(L, T);
+  if (need > MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ENOSPC, "moe_forward_static: T = %d needs %zu bytes of scratch, above its "
+                "%zu-byte maximum", T, need, (size_t)MOE_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  MOE_TRY(static_scratch(&ws));
+  Marker none;
+  return forward_impl(L, T, x, logits_in, token_ids, out_f32, out_bf16, topk_idx_out, topk_w_out,
+                      ws, MOE_STATIC_SCRATCH_BYTES, nullptr, stream, none);
 }
 
 int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
