@@ -53,6 +53,8 @@ def _args():
                     help="comma-separated extra workloads measured after the headline")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--extra-warmup", type=int, default=20)
+    ap.add_argument("--no-cache-curve", action="store_true",
+                    help="skip the routed-expert cache's decode-vs-hit-rate curve")
     ap.add_argument("--no-probes", action="store_true",
                     help="skip the HBM / matrix-core peak probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -525,6 +527,86 @@ def measure(wname, args, dev, headline):
     return res, host, w, L
 
 
+def cache_curve(dev, hit_rates=(0.0, 0.25, 0.5, 0.75, 0.875, 1.0), n_slots=64, steps=64,
+                seed=0):
+    """decode_b1 with the routed experts in pinned host memory and n_slots of
+    them resident in HBM (moe_forward_cached): tokens/s against the hit rate.
+    Each step's logits pick round(h k) experts among the resident ones and
+    the rest among the others, planned eagerly from the cache's own table
+    (the device decides; the plan only reads it back between steps), then
+    the same sequence is replayed from an emptied-and-warmed cache and timed
+    step by step.  Roofline: the host link, measured as a pinned host -> HBM
+    copy; each miss moves one expert (7,077,888 B at this layer)."""
+    import torch
+
+    import routed_expert_ffn_router_amd as moe
+    import synth
+
+    w = synth.WORKLOADS["decode_b1"]
+    host = synth.gen_layer(w.layer, seed)
+    cl = moe.CachedLayer(host, n_slots, dev)
+    E, k = w.layer.E, w.layer.k
+    per_expert = host.routed_bytes_per_expert()
+    # the host link: one 512 MiB pinned -> device copy
+    src = torch.empty(512 << 20, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ts = []
+    for _ in range(4):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    link = (512 << 20) / min(ts[1:]) / 1e9
+    del src, dst
+    rng = np.random.default_rng(seed)
+    xs = [torch.from_numpy(synth.gen_x(w.layer.H, 1, seed, step=i).view(np.int16)).to(dev)
+          for i in range(16)]
+    curve = []
+    for h in hit_rates:
+        n_hit = int(round(h * k))
+        cl.reset()
+        seq = []
+        for s in range(n_slots // k + steps):
+            res = cl.resident()
+            warm = s < n_slots // k
+            pool_res = np.flatnonzero(res >= 0)
+            pool_non = np.flatnonzero(res < 0)
+            nh = 0 if warm else n_hit
+            chosen = np.concatenate([rng.choice(pool_res, nh, replace=False),
+                                     rng.choice(pool_non, k - nh, replace=False)])
+            lg = rng.standard_normal(E).astype(np.float32) - 10.0
+            lg[chosen] = 10.0 - np.arange(k, dtype=np.float32)
+            lt = torch.from_numpy(lg[None, :]).to(dev)
+            seq.append(lt)
+            cl(xs[s % 16], lt)
+        cl.reset()
+        nw = n_slots // k
+        for s in range(nw):
+            cl(xs[s % 16], seq[s])
+        torch.cuda.synchronize()
+        h0, m0 = cl.counts()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            cl(xs[(nw + i) % 16], seq[nw + i])
+            b.record()
+        torch.cuda.synchronize()
+        h1, m1 = cl.counts()
+        t = float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+        miss_bytes = (m1 - m0) / steps * per_expert
+        curve.append({"hit_rate": (h1 - h0) / max(h1 - h0 + m1 - m0, 1), "us_per_step": t * 1e6,
+                      "tokens_per_s": 1.0 / t, "miss_bytes_per_step": miss_bytes,
+                      "host_link_gbps": miss_bytes / t / 1e9,
+                      "host_link_frac": miss_bytes / t / 1e9 / link})
+    del cl
+    torch.cuda.empty_cache()
+    return {"n_slots": n_slots, "E": E, "k": k, "expert_bytes": per_expert,
+            "host_link_probe_gbps": link, "steps": steps, "curve": curve}
+
+
 def add_probed(roof, peaks):
     """Beside the spec peak: the probed one and the fraction of it."""
     if not peaks:
@@ -574,6 +656,10 @@ def main():
         if not args.no_cpu_baseline and xw.T >= 2048:
             r["cpu_baseline"] = cpu_baseline(xhost, xw, 0, args.cpu_seconds / 2, max_tokens=32)
         extras[name] = r
+    if not args.no_cache_curve:
+        _LAYERS.clear()
+        torch.cuda.empty_cache()
+        extras["decode_b1_expert_cache"] = cache_curve(dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host, w, 0, args.cpu_seconds)

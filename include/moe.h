@@ -283,6 +283,41 @@ int moe_forward_static(const moe_layer *layer, int T, const uint16_t *x, const f
                        const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                        int32_t *topk_idx_out, float *topk_w_out, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* A residency cache of routed experts in HBM for one-token decode, filled
+ * from pinned host memory: the analogue of the pages' streaming of routed
+ * experts from SSD when the model exceeds memory (hysenlabs.com ds4 page,
+ * "SSD streaming"; baiwuji.top ds4 article, "Core features" item 2: the few
+ * experts a generated token picks are read from the slower tier).
+ *   - The layer passed to moe_forward_cached holds all E experts' gate, up
+ *     and down in host memory from hipHostMalloc (mapped, so the device can
+ *     read it); router and shared expert are in device memory as usual.
+ *   - slot_gate/up/down: the same formats for n_slots experts in device
+ *     memory: the slots.  n_slots >= k.  Every plane's bytes per expert must
+ *     be a multiple of 16 (MOE_EUNSUPPORTED otherwise).
+ *   - state: device int32 [moe_cache_state_ints(E, n_slots)], emptied by
+ *     moe_cache_reset.  state[2] and state[3] count hits and misses so far;
+ *     state[4 + e] is the slot holding expert e, or -1.
+ * Each step the device itself selects the k experts (as moe_route does),
+ * looks them up, gives each miss the least recently used slot that no
+ * expert of this step holds (lowest slot on ties), copies the missed
+ * experts' bytes from host memory into their slots, then runs the routed
+ * FFN on the slots -- no host round trip, so the call can be captured in a
+ * HIP graph.  Results are identical to moe_forward's.  T must be 1 and the
+ * layer one that moe_forward runs in its one-token launches
+ * (MOE_EUNSUPPORTED otherwise). */
+typedef struct {
+  int32_t n_slots;
+  moe_weights slot_gate, slot_up, slot_down;
+  int32_t *state;
+} moe_expert_cache;
+size_t moe_cache_state_ints(int E, int n_slots);
+int moe_cache_reset(const moe_expert_cache *cache, int E, void *stream);
+int moe_forward_cached(const moe_layer *layer, const moe_expert_cache *cache, int T,
+                       const uint16_t *x, const float *logits_in, const int64_t *token_ids,
+                       float *out_f32, uint16_t *out_bf16, int32_t *topk_idx_out,
+                       float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
+
 /* moe_forward_marked: moe_forward for measurement tools.  Each kernel the
  * call enqueues (up to max_marks of them) is launched so that it records the
  * caller's events marks[i].start and marks[i].stop (hipEvent_t passed as

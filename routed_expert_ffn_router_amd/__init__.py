@@ -47,6 +47,11 @@ class SideStream(C.Structure):
     _fields_ = [("stream", C.c_void_p), ("fork", C.c_void_p), ("join", C.c_void_p)]
 
 
+class ExpertCache(C.Structure):
+    _fields_ = [("n_slots", C.c_int32), ("slot_gate", Weights), ("slot_up", Weights),
+                ("slot_down", Weights), ("state", C.c_void_p)]
+
+
 class Mark(C.Structure):
     _fields_ = [("start", C.c_void_p), ("stop", C.c_void_p), ("name", C.c_char_p)]
 
@@ -93,6 +98,11 @@ def lib():
         L.moe_forward_marked.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          C.POINTER(Mark), i32, C.POINTER(i32), vp]
         L.moe_forward_static.argtypes = [C.POINTER(Layer), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_cache_state_ints.restype = sz
+        L.moe_cache_state_ints.argtypes = [i32, i32]
+        L.moe_cache_reset.argtypes = [C.POINTER(ExpertCache), i32, vp]
+        L.moe_forward_cached.argtypes = [C.POINTER(Layer), C.POINTER(ExpertCache), i32, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, sz, vp]
         L.moe_probe_read_blocks.restype = i32
         L.moe_probe_read_blocks.argtypes = [sz]
         L.moe_probe_hbm_read.argtypes = [vp, sz, vp, vp]
@@ -389,6 +399,80 @@ class Forward:
                                         _ptr(self.idx), _ptr(self.w), _ptr(self.ws), self.ws.numel(),
                                         marks, len(events), C.byref(n), _stream()))
         return [marks[i].name.decode() for i in range(n.value)]
+
+
+class CachedLayer:
+    """A layer whose routed experts live in pinned host memory, with a pool of
+    n_slots expert slots in device memory and the cache state
+    (moe_expert_cache); forward() runs moe_forward_cached on one token."""
+
+    def __init__(self, host, n_slots, device="cuda", route_mode=ROUTE_SOFTMAX_TOPK):
+        s = host.spec
+        dev = torch.device(device)
+
+        def pinned(a):
+            return torch.from_numpy(a.reshape(-1).view("uint8").copy()).pin_memory()
+
+        cb = None
+        if host.codebook is not None:
+            cb = torch.from_numpy(host.codebook.reshape(-1).view("uint8").copy()).to(dev)
+        projs, slots = [], []
+        for p in (host.gate, host.up, host.down):
+            c = cb if p.fmt == FMT_VQ2 else None
+            hd = pinned(p.data)
+            hs = None if p.scales is None else pinned(p.scales)
+            projs.append(DeviceProj(p.fmt, p.E, p.N, p.K, hd, hs, c))
+            sd = torch.empty(hd.numel() // p.E * n_slots, dtype=torch.uint8, device=dev)
+            ss = None if hs is None else torch.empty(hs.numel() // p.E * n_slots,
+                                                     dtype=torch.uint8, device=dev)
+            slots.append(DeviceProj(p.fmt, n_slots, p.N, p.K, sd, ss, c))
+
+        def u16(a):
+            return None if a is None else torch.from_numpy(a.view("int16").copy()).to(dev)
+
+        self.layer = DeviceLayer(s.H, s.I, s.E, s.k, route_mode, u16(host.w_router), *projs,
+                                 u16(host.shared_gate), u16(host.shared_up),
+                                 u16(host.shared_down))
+        self.slots = slots
+        self.n_slots, self.E = n_slots, s.E
+        self.state = torch.empty(int(lib().moe_cache_state_ints(s.E, n_slots)),
+                                 dtype=torch.int32, device=dev)
+        self.c = ExpertCache(n_slots, slots[0].c, slots[1].c, slots[2].c, _ptr(self.state))
+        self.f = Forward(self.layer, 1, dev, side_stream=False)
+        self.reset()
+
+    def reset(self):
+        """moe_cache_reset: no expert resident."""
+        _check(lib().moe_cache_reset(C.byref(self.c), self.E, _stream()))
+
+    def __call__(self, x, logits_in=None, token_ids=None):
+        """moe_forward_cached -> the layer's output fp32 [1, H] (and .idx, .w)."""
+        _dev(x, BF16, "x")
+        _dev(logits_in, torch.float32, "logits_in")
+        _dev(token_ids, torch.int64, "token_ids")
+        f = self.f
+        _check(lib().moe_forward_cached(C.byref(self.layer.c), C.byref(self.c), x.shape[0],
+                                        _ptr(x), _ptr(logits_in), _ptr(token_ids), _ptr(f.out),
+                                        None, _ptr(f.idx), _ptr(f.w), _ptr(f.ws), f.ws.numel(),
+                                        _stream()))
+        return f.out
+
+    @property
+    def idx(self):
+        return self.f.idx
+
+    @property
+    def w(self):
+        return self.f.w
+
+    def resident(self):
+        """Host copy of the expert -> slot map (-1: not resident)."""
+        return self.state[4:4 + self.E].cpu().numpy()
+
+    def counts(self):
+        """(hits, misses) so far."""
+        h = self.state[2:4].cpu().numpy()
+        return int(h[0]), int(h[1])
 
 
 def forward_static(layer, x, out, idx, w, logits_in=None, token_ids=None, out_bf16=None):

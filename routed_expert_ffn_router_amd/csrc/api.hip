@@ -707,6 +707,109 @@ int moe_forward_static(const moe_layer *L, int T, const uint16_t *x, const float
                       ws, MOE_STATIC_SCRATCH_BYTES, nullptr, stream, none);
 }
 
+// ---------------------------------------------------------------------------
+// the routed-expert residency cache
+// ---------------------------------------------------------------------------
+
+size_t moe_cache_state_ints(int E, int n_slots) {
+  if (E < 1 || n_slots < 1) return 0;
+  return cache_state_ints(E, n_slots);
+}
+
+static int check_cache(const moe_expert_cache *c, int E, int k) {
+  if (!c || !c->state) return fail(MOE_EINVAL, "cache: null cache or state");
+  if (c->n_slots < k || c->n_slots > 1024)
+    return fail(MOE_EINVAL, "cache: n_slots = %d outside [k = %d, 1024]", c->n_slots, k);
+  return MOE_OK;
+}
+
+int moe_cache_reset(const moe_expert_cache *c, int E, void *stream) {
+  if (E < 1 || E > 1024) return fail(MOE_EINVAL, "E = %d outside [1, 1024]", E);
+  MOE_TRY(check_cache(c, E, 1));
+  return hip_check(launch_cache_reset(E, c->n_slots, c->state, as_stream(stream)), "cache reset");
+}
+
+// the byte planes of a projection, host (all experts) and slots
+static int cache_planes(const moe_weights &host, const moe_weights &slot, CacheStep &cs) {
+  const size_t pd = expert_data_bytes(host.fmt, host.rows, host.cols);
+  const size_t ps = expert_scale_bytes(host.fmt, host.rows, host.cols);
+  const void *planes[2] = {host.data, host.scales};
+  void *dplanes[2] = {const_cast<void *>(slot.data), const_cast<void *>(slot.scales)};
+  const size_t per[2] = {pd, ps};
+  for (int i = 0; i < 2; i++) {
+    if (!per[i]) continue;
+    if (per[i] % 16 || !aligned(planes[i], 16) || !aligned(dplanes[i], 16))
+      return fail(MOE_EUNSUPPORTED, "cache: plane bytes per expert (%zu) or bases not 16-byte "
+                  "aligned", per[i]);
+    void *dev = nullptr;
+    MOE_TRY(hip_check(hipHostGetDevicePointer(&dev, const_cast<void *>(planes[i]), 0),
+                      "cache: host weights must come from hipHostMalloc"));
+    cs.src[cs.n_planes] = static_cast<const uint8_t *>(dev);
+    cs.dst[cs.n_planes] = static_cast<uint8_t *>(dplanes[i]);
+    cs.per_bytes[cs.n_planes] = per[i];
+    cs.n_planes++;
+  }
+  return MOE_OK;
+}
+
+int moe_forward_cached(const moe_layer *L, const moe_expert_cache *c, int T, const uint16_t *x,
+                       const float *logits_in, const int64_t *token_ids, float *out_f32,
+                       uint16_t *out_bf16, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  MOE_TRY(check_layer(L));
+  MOE_TRY(check_cache(c, L->E, L->k));
+  const int C = c->n_slots;
+  MOE_TRY(check_ffn_weights(C, L->H, L->I, &c->slot_gate, &c->slot_up, &c->slot_down));
+  if (c->slot_gate.fmt != L->gate.fmt || c->slot_down.fmt != L->down.fmt ||
+      (c->slot_gate.fmt == MOE_FMT_VQ2 && c->slot_gate.codebook != L->gate.codebook))
+    return fail(MOE_EINVAL, "cache: slots differ in format (or codebook) from the layer");
+  if (T == 0) return MOE_OK;
+  if (T != 1 || !fwd_decode1(L, T))
+    return fail(MOE_EUNSUPPORTED, "cache: one-token decode layers only");
+  if (!x || !out_f32) return fail(MOE_EINVAL, "null x or out");
+  if (!aligned(x, 16) || !aligned(out_f32, 16) || (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "x/out misaligned");
+  if (L->route_mode == MOE_ROUTE_HASH && !token_ids)
+    return fail(MOE_EINVAL, "hash routing needs token_ids");
+  const size_t need = moe_forward_workspace(L, T);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ENOSPC, "forward workspace: %zu bytes < %zu", ws_bytes, need);
+  Carver cv(ws);
+  FwdBufs b = carve_fwd(cv, L, T, false, false, false);
+  CacheStep cs{};
+  MOE_TRY(cache_planes(L->gate, c->slot_gate, cs));
+  MOE_TRY(cache_planes(L->up, c->slot_up, cs));
+  MOE_TRY(cache_planes(L->down, c->slot_down, cs));
+  DecodeArgs a{};
+  const int H = L->H, I = L->I, E = L->E, k = L->k;
+  a.H = H, a.I = I, a.E = E, a.k = k, a.mode = L->route_mode;
+  a.Is = has_shared(L) ? L->I_shared : 0;
+  a.x = x, a.w_router = L->w_router, a.logits_in = logits_in, a.tid = token_ids;
+  a.gate = view_of(c->slot_gate), a.up = view_of(c->slot_up), a.down = view_of(c->slot_down);
+  if (a.Is) {
+    a.sg = bf16_view(L->shared_gate, a.Is, H);
+    a.su = bf16_view(L->shared_up, a.Is, H);
+    a.sd = bf16_view(L->shared_down, H, a.Is);
+  }
+  a.logits = b.logits, a.a_sh = b.a_sh, a.a = b.a, a.shared_y = b.shared_y;
+  a.a_sh_hi = reinterpret_cast<uint16_t *>(b.a_sh);
+  a.a_sh_lo = a.Is ? a.a_sh_hi + a.Is : nullptr;
+  a.a_hi = reinterpret_cast<uint16_t *>(b.a);
+  a.a_lo = a.a_hi + (size_t)k * I;
+  a.topk_idx = topk_idx_out ? topk_idx_out : b.idx;
+  a.topk_w = topk_w_out ? topk_w_out : b.w;
+  a.out = out_f32, a.out_bf16 = out_bf16;
+  a.steer_dir = L->steer_dir, a.steer_alpha = L->steer_alpha;
+  a.slot_idx = c->state + cache_slot_idx_offset(E, C);
+  cs.mode = L->route_mode, cs.E = E, cs.C = C, cs.k = k;
+  cs.logits = logits_in ? logits_in : b.logits;
+  cs.tid = token_ids;
+  cs.state = c->state;
+  cs.topk_idx = a.topk_idx, cs.topk_w = a.topk_w;
+  Marker none;
+  return hip_check(launch_decode1(a, as_stream(stream), mark_cb, &none, &cs), "cached decode");
+}
+
 int moe_forward_marked(const moe_layer *L, int T, const uint16_t *x, const float *logits_in,
                        const int64_t *token_ids, float *out_f32, uint16_t *out_bf16,
                        int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,

@@ -138,7 +138,12 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       if (lane == 0) atomicAdd(&s_ready, 1);
     }
-  if (wave == 0) {
+  if (wave == 0 && p.slot_idx) {
+    // the expert cache planned the choices and their slots
+    if (lane < p.k) s_e[lane] = p.slot_idx[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) atomicAdd(&s_ready, 1);
+  } else if (wave == 0) {
     // the selection is the block's critical path: its wave issues first
     __builtin_amdgcn_s_setprio(3);
     int e;
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   constexpr int ST = steps_for<RFMT, RSPL>();
   const int j = blockIdx.x / p.tiles_per_expert, tile = blockIdx.x % p.tiles_per_expert;
   const int row_base = (tile * kDecWaves + wave) * ST;
-  const int e_sel = min(max(__builtin_amdgcn_readfirstlane(s_e[j]), 0), p.E - 1);
+  const int e_sel = min(max(__builtin_amdgcn_readfirstlane(s_e[j]), 0), p.gate.E - 1);
   // every routed row pair's loads go out at once (MXFP4's larger chunks: two)
   constexpr int kRPF = RFMT == MOE_FMT_MXFP4 ? 2 : ST;
   gateup_rows<RFMT, RSPL, 64, ST, 1, kRPF, kCopies>(p.gate, p.up, p.H, p.I, p.x, e_sel, j, j + 1,
@@ -248,7 +253,8 @@ __global__ __launch_bounds__(kP3Threads) void k_dec_p3(DecodeArgs p) {
           av[0].load(p.a + (size_t)j * p.I, lane);
       };
       if constexpr (kAFirst) load_a();
-      const int e = __builtin_amdgcn_readfirstlane(p.topk_idx[j]);
+      const int32_t *eidx = p.slot_idx ? p.slot_idx : p.topk_idx;  // expert, or its cache slot
+      const int e = __builtin_amdgcn_readfirstlane(eidx[j]);
       const float wj = __builtin_bit_cast(
           float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.topk_w[j])));
       Chunk<DFMT, DSPL, 64> c[PF];
@@ -342,7 +348,7 @@ bool decode1_supported(int H, int I, int Is, int k) {
 }
 
 hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, const char *),
-                          void *mark_ctx) {
+                          void *mark_ctx, const CacheStep *cache) {
   const int hs = spl_of(a.H), is = spl_of(a.I), ss = a.Is ? spl_of(a.Is) : 2;
   // p1: one router row per block and one shared gate/up row pair per wave
   a.nb_router = a.logits_in ? 0 : a.E;
@@ -360,6 +366,10 @@ hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, cons
     const int g1 = max(a.nb_router, a.nb_shared_gu);
     e = hs == 4 ? launch(k_dec_p1<4>, dim3(g1), dim3(kP1Threads), s, a)
                 : launch(k_dec_p1<2>, dim3(g1), dim3(kP1Threads), s, a);
+    if (e != hipSuccess) return e;
+  }
+  if (cache) {
+    e = launch_cache_step(*cache, s, mark, mark_ctx);
     if (e != hipSuccess) return e;
   }
   mark(mark_ctx, "decode_p2");

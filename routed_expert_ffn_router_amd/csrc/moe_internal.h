@@ -180,12 +180,35 @@ struct DecodeArgs {
   uint16_t *out_bf16;        // optional [H]
   const float *steer_dir;    // optional [H]: out += steer_alpha * steer_dir
   float steer_alpha;
+  const int32_t *slot_idx;   // optional [k]: weight index of choice j (expert cache slots);
+                             // p2 then takes it instead of selecting
   int nb_router, nb_shared_gu, nb_routed, tiles_per_expert;
 };
 
 bool decode1_supported(int H, int I, int Is, int k);
+struct CacheStep;
+// p1, then (with a cache) the cache's plan and fill, then p2 and p3
 hipError_t launch_decode1(DecodeArgs a, hipStream_t s, void (*mark)(void *, const char *),
-                          void *mark_ctx);
+                          void *mark_ctx, const CacheStep *cache = nullptr);
+
+// routed-expert residency cache (cache.hip) ----------------------------------
+struct CacheStep {
+  int mode, E, C, k;
+  const float *logits;
+  const int64_t *tid;
+  int32_t *state;       // cache_state_ints(E, C) ints
+  int32_t *topk_idx;    // [k]
+  float *topk_w;        // [k]
+  int n_planes;         // byte planes of an expert: gate/up/down data and scales
+  const uint8_t *src[6];  // host planes of all E experts (device-accessible pointers)
+  uint8_t *dst[6];        // slot planes of the C slots
+  size_t per_bytes[6];    // bytes of one expert in each plane (multiples of 16)
+};
+size_t cache_state_ints(int E, int C);
+int cache_slot_idx_offset(int E, int C);
+hipError_t launch_cache_reset(int E, int C, int32_t *state, hipStream_t s);
+hipError_t launch_cache_step(const CacheStep &c, hipStream_t s,
+                             void (*mark)(void *, const char *), void *mark_ctx);
 
 // combine -----------------------------------------------------------------
 hipError_t launch_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_pos,

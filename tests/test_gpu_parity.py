@@ -1004,3 +1004,111 @@ def test_forward_verify_graph_replay(dev, q2, dq2, T):
     f = moe.Forward(dq2, T, dev)
     xs = [t16(synth.gen_x(4096, T, seed=120 + T + i), dev) for i in range(3)]
     _graph_replays(f, xs)
+
+
+# --------------------------------------------------------------------------
+# the routed-expert residency cache: experts in pinned host memory, a pool of
+# slots in HBM, decided and filled on the device
+# --------------------------------------------------------------------------
+
+def _logits_for(E, chosen, rng):
+    """Logits whose top-len(chosen) are `chosen`, in that order."""
+    lg = rng.standard_normal(E).astype(np.float32) - 10.0
+    lg[chosen] = 10.0 - np.arange(len(chosen), dtype=np.float32)
+    return lg[None, :]
+
+
+def _pick(rng, resident, E, k, n_hit):
+    res = np.flatnonzero(resident >= 0)
+    non = np.flatnonzero(resident < 0)
+    return np.concatenate([rng.choice(res, n_hit, replace=False),
+                           rng.choice(non, k - n_hit, replace=False)])
+
+
+@pytest.fixture(scope="module")
+def cached_q2(q2, dev):
+    return moe.CachedLayer(q2, 32, dev)
+
+
+@pytest.mark.parametrize("hit", [0.0, 0.5, 1.0])
+def test_forward_cached_hit_rates(dev, q2, dq2, cached_q2, hit):
+    """Steps at a controlled hit rate (the chosen experts picked from the
+    resident ones and the others): every step's output, choices and weights
+    equal moe_forward's bit for bit, the counters record exactly the planned
+    hits and misses, and a step matches the oracle."""
+    cl = cached_q2
+    cl.reset()
+    rng = np.random.default_rng(int(hit * 10) + 3)
+    E, k = 256, 8
+    # warm: fill the 32 slots with 4 steps of misses
+    for s in range(4):
+        chosen = _pick(rng, cl.resident(), E, k, 0)
+        x = t16(synth.gen_x(4096, 1, seed=200 + s), dev)
+        cl(x, torch.from_numpy(_logits_for(E, chosen, rng)).to(dev))
+    assert (cl.resident() >= 0).sum() == 32
+    n_hit = int(round(hit * k))
+    for s in range(6):
+        h0, m0 = cl.counts()
+        chosen = _pick(rng, cl.resident(), E, k, n_hit)
+        lg = _logits_for(E, chosen, rng)
+        x = synth.gen_x(4096, 1, seed=300 + s)
+        lt, xt = torch.from_numpy(lg).to(dev), t16(x, dev)
+        out = tnp(cl(xt, lt)).copy()
+        idx, w = tnp(cl.idx).copy(), tnp(cl.w).copy()
+        ref, ridx, rw = moe.forward(dq2, xt, lt)
+        assert np.array_equal(out.view(np.uint32), tnp(ref).view(np.uint32)), s
+        assert np.array_equal(idx, tnp(ridx)) and np.array_equal(w, tnp(rw))
+        assert list(idx.reshape(-1)) == list(chosen)
+        h1, m1 = cl.counts()
+        assert (h1 - h0, m1 - m0) == (n_hit, k - n_hit), (s, h1 - h0, m1 - m0)
+        res = cl.resident()
+        assert (res[chosen] >= 0).all() and len(set(res[chosen])) == k
+    oref, oidx, _ = oracle.LayerRef(q2).forward(x, lg)
+    assert np.array_equal(idx, oidx)
+    assert normwise(out, oref) < TOL
+
+
+def test_forward_cached_router_hash_and_graph(dev, q2, dq2, cached_q2):
+    """Router logits (computed by the layer's own p1) and hash routing through
+    the cache; a captured step replayed with eager steps between the replays
+    equals the eager result every time (hits or misses)."""
+    cl = cached_q2
+    cl.reset()
+    for s in range(5):
+        xt = t16(synth.gen_x(4096, 1, seed=400 + s), dev)
+        out = tnp(cl(xt)).copy()
+        ref, _, _ = moe.forward(dq2, xt)
+        assert np.array_equal(out.view(np.uint32), tnp(ref).view(np.uint32)), s
+    hl = moe.CachedLayer.__new__(moe.CachedLayer)
+    hl.__dict__.update(cl.__dict__)
+    hl.layer = cl.layer.with_route_mode(moe.ROUTE_HASH)
+    hl.f = moe.Forward(hl.layer, 1, dev, side_stream=False)
+    dh = dq2.with_route_mode(moe.ROUTE_HASH)
+    for s in range(3):
+        xt = t16(synth.gen_x(4096, 1, seed=500 + s), dev)
+        tid = torch.from_numpy(synth.gen_token_ids(1, seed=s)).to(dev)
+        out = tnp(hl(xt, None, tid)).copy()
+        ref, _, _ = moe.forward(dh, xt, None, tid)
+        assert np.array_equal(out.view(np.uint32), tnp(ref).view(np.uint32)), s
+    xs = [t16(synth.gen_x(4096, 1, seed=600 + i), dev) for i in range(3)]
+    refs = [tnp(moe.forward(dq2, x)[0]).copy() for x in xs]
+    xb = xs[0].clone()
+    cl(xb)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        cl(xb)
+    torch.cuda.current_stream().wait_stream(s_)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        cl(xb)
+    for rep in range(2):
+        for i, x in enumerate(xs):
+            xb.copy_(x)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(tnp(cl.f.out).view(np.uint32), refs[i].view(np.uint32)), (rep, i)
+            cl(xs[(i + 1) % 3])
+            torch.cuda.synchronize()
