@@ -485,6 +485,345 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Tiles of 64 or 128 bucket rows: the same block shape on the 32 x 32 x 16
+// matrix instructions, which run this chip's fp16 / bf16 products about 1.6
+// times faster than the 16 x 16 x 32 ones (measured with the matrix-core
+// probe).  Operand layout (v_mfma_f32_32x32x16_{f16,bf16}): lane l holds 8
+// consecutive reduction slots 8 (l / 32) + [0, 8) of A row l % 32 and of B
+// column l % 32; result register i of lane l is row 8 (i / 4) + 4 (l / 32) +
+// i % 4, column l % 32.
+//
+// Reduction slots: lane half h = l / 32 covers, over a 256-group's 4 stages,
+// the contiguous run 128 h + [0, 128) of its weight row, 32 per stage, 8 per
+// instruction; the A stage in LDS holds, in column c, k = 256 G + 128 (c /
+// 32) + 32 S + c % 32, so that lane (row, h) reads columns 32 h + 8 t of its
+// row for instruction t.  Q2K weights keep the swap12 pairing within each
+// group of 4 (the A operand is stored in that order where it is produced).
+// ---------------------------------------------------------------------------
+typedef float f32x16v_t __attribute__((ext_vector_type(16)));
+
+template <int OP>
+__device__ __forceinline__ f32x16v_t mfma32(uint4 a, uint4 b, f32x16v_t c) {
+  if constexpr (OP == kOpBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// one lane's run of 128 weights of a row in a 256-group: raw bits -> 16
+// operand pairs per stage (stage S: the run's weights 32 S .. 32 S + 31)
+template <int FMT, int OP>
+struct BRun {
+  uint32_t q[FMT == MOE_FMT_MXFP4 ? 16 : 8];
+  uint32_t s0, s1, s2;  // VQ2: scale; Q2K: 8 scale/min bytes, d|dmin; MXFP4: 4 E8M0 bytes
+
+  // k0: first column of the run (256 G + 128 h)
+  __device__ __forceinline__ void load(const WView &w, int e, int row, int k0) {
+    const uint32_t db = (uint32_t)expert_data_bytes(FMT, w.N, w.K);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(w.data + (size_t)e * db, db);
+    if constexpr (FMT == MOE_FMT_VQ2) {
+      const uint32_t sb = (uint32_t)expert_scale_bytes(FMT, w.N, w.K);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.scales + (size_t)e * sb, sb);
+      const uint32_t vo = (uint32_t)row * (uint32_t)(w.K / 4) + (uint32_t)k0 / 4;
+      const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+      q[0] = a.x, q[1] = a.y, q[2] = a.z, q[3] = a.w, q[4] = b.x, q[5] = b.y, q[6] = b.z, q[7] = b.w;
+      s0 = buf_u16(rs, ((uint32_t)row * (uint32_t)(w.K / 256) + (uint32_t)k0 / 256) * 2u, 0);
+    } else if constexpr (FMT == MOE_FMT_Q2K) {
+      const uint32_t blk = ((uint32_t)row * (uint32_t)(w.K / 256) + (uint32_t)k0 / 256) * kQ2KBytes;
+      const uint32_t j = (k0 % 256) / 16;  // first of the 8 sub-blocks
+#pragma unroll
+      for (int i = 0; i < 8; i++) q[i] = buf_u32(r, blk + 16 + 4 * (j + i), 0);
+      s0 = buf_u32(r, blk + j, 0);
+      s1 = buf_u32(r, blk + j + 4, 0);
+      s2 = buf_u32(r, blk + 80, 0);
+    } else {  // MXFP4
+      const uint32_t sb = (uint32_t)expert_scale_bytes(FMT, w.N, w.K);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.scales + (size_t)e * sb, sb);
+      const uint32_t vo = (uint32_t)row * (uint32_t)(w.K / 2) + (uint32_t)k0 / 2;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const u32x4_t a = buf_u128(r, vo + 16 * i, 0);
+        q[4 * i] = a.x, q[4 * i + 1] = a.y, q[4 * i + 2] = a.z, q[4 * i + 3] = a.w;
+      }
+      s0 = buf_u32(rs, (uint32_t)row * (uint32_t)(w.K / 32) + (uint32_t)k0 / 32, 0);
+    }
+  }
+
+  __device__ __forceinline__ void decode(int S, uint32_t (&out)[16], const uint2 *cb) const {
+    if constexpr (FMT == MOE_FMT_VQ2) {
+      const f16x2_t d2 = {__builtin_bit_cast(_Float16, (uint16_t)s0),
+                          __builtin_bit_cast(_Float16, (uint16_t)s0)};
+#pragma unroll
+      for (int c = 0; c < 8; c++) {
+        const uint2 v = cb[((q[2 * S + c / 4] >> (8 * (c % 4))) & 255u) * kNCopy];
+        out[2 * c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * d2);
+        out[2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * d2);
+      }
+    } else if constexpr (FMT == MOE_FMT_Q2K) {
+      const float d = f16_bits_to_f32(s2 & 0xFFFFu), dmin = f16_bits_to_f32(s2 >> 16);
+#pragma unroll
+      for (int sb = 0; sb < 2; sb++) {
+        const int sub = 2 * S + sb;  // sub-block of the run: scale byte `sub`
+        const uint32_t scm = ((sub < 4 ? s0 : s1) >> (8 * (sub % 4))) & 255u;
+        const float ds = d * (float)(scm & 15u), ms = dmin * (float)(scm >> 4);
+        const f16x2_t ds2 = {(_Float16)ds, (_Float16)ds};
+        const f16x2_t nms2 = {(_Float16)(-ms), (_Float16)(-ms)};
+        const uint32_t x = q[sub];
+        const uint32_t nl = x & 0x33333333u, nh = (x >> 2) & 0x33333333u;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const f16x2_t p0 = __builtin_bit_cast(f16x2_t, q2_pair(nl, b));
+          const f16x2_t p1 = __builtin_bit_cast(f16x2_t, q2_pair(nh, b));
+          out[8 * sb + 2 * b] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(p0, ds2, nms2));
+          out[8 * sb + 2 * b + 1] =
+              __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(p1, ds2, nms2));
+        }
+      }
+    } else {  // MXFP4: one E8M0 scale per stage (32 weights)
+      const float sc = e8m0_to_f32((s0 >> (8 * S)) & 255u);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const uint32_t v = q[4 * S + j];
+        if constexpr (OP == kOpBF16) {
+          out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
+          out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
+          out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
+          out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
+        } else {
+          out[4 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 0));
+          out[4 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 1));
+          out[4 * j + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 2));
+          out[4 * j + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, sc, 3));
+        }
+      }
+    }
+  }
+};
+
+// bf16 weights: one stage's 32 weights of the run (64 bytes)
+template <int OP>
+struct BStageBf16x32 {
+  uint32_t q[16];
+  __device__ __forceinline__ void load(const WView &w, int e, int row, int k) {
+    const uint32_t db = (uint32_t)expert_data_bytes(MOE_FMT_BF16, w.N, w.K);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(w.data + (size_t)e * db, db);
+    const uint32_t vo = ((uint32_t)row * (uint32_t)w.K + (uint32_t)k) * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const u32x4_t a = buf_u128(r, vo + 16 * i, 0);
+      q[4 * i] = a.x, q[4 * i + 1] = a.y, q[4 * i + 2] = a.z, q[4 * i + 3] = a.w;
+    }
+  }
+  __device__ __forceinline__ void decode(uint32_t (&out)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 16; i++) out[i] = OP == kOpF16 ? bf16x2_to_f16x2(q[i]) : q[i];
+  }
+};
+
+// A stage for the 32-wide layout: thread t stages row t / (256 / BM), LDS
+// columns acol .. acol + 64 / (256 / BM) - 1, in runs of 16: LDS column c is
+// k = kb + 128 (c / 32) + c % 32 with kb = 256 G + 32 S
+template <int BM>
+struct AStage32 {
+  static constexpr int kCPT = 64 / (kGemmThreads / BM);  // 16 (BM 64) or 32 (BM 128)
+  uint32_t raw[kCPT / 2];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row_off, int kb, int acol) {
+#pragma unroll
+    for (int j = 0; j < kCPT / 16; j++) {
+      const int c = acol + 16 * j;
+      const uint32_t vo = row_off + (uint32_t)(kb + 128 * (c / 32) + c % 32) * 2u;
+      const u32x4_t a = buf_u128(r, vo, 0), b = buf_u128(r, vo + 16, 0);
+      raw[8 * j] = a.x, raw[8 * j + 1] = a.y, raw[8 * j + 2] = a.z, raw[8 * j + 3] = a.w;
+      raw[8 * j + 4] = b.x, raw[8 * j + 5] = b.y, raw[8 * j + 6] = b.z, raw[8 * j + 7] = b.w;
+    }
+  }
+  __device__ __forceinline__ void store(uint32_t *dst) const {
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < kCPT / 8; i++)
+      d4[i] = make_uint4(raw[4 * i], raw[4 * i + 1], raw[4 * i + 2], raw[4 * i + 3]);
+  }
+};
+
+template <int MODE, int FMT, int OP, int BM>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm32(GemmArgs p) {
+  static_assert(BM == 64 || BM == 128, "32-row blocks");
+  constexpr int MB = BM / 32;  // MFMA row blocks
+  constexpr int NB = 2;        // 32-column blocks per wave (64 weight rows)
+  constexpr int kPA = 4;       // A stages in flight (one group)
+  constexpr bool kGroupB = FMT != MOE_FMT_BF16;
+  __shared__ uint32_t s_a[2][BM * kLdsRowW];
+  __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
+  // XCD-aware order, as in k_gemm
+  const uint32_t nbx = gridDim.x, nby = gridDim.y;
+  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t jx = bid >> 3;
+  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
+  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
+  if (ti >= p.tiles[0]) return;
+  const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
+  const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
+  const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;  // MFMA row / column within a block; k half
+  const int n0 = bx * block_cols<MODE, FMT>();
+
+  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, kNCopy copies
+    const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[tid];
+    uint32_t hv[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      hv[j] = pack_h2((float)(int)(int8_t)((cw >> (16 * j)) & 255u),
+                      (float)(int)(int8_t)((cw >> (16 * j + 8)) & 255u));
+#pragma unroll
+    for (int j = 0; j < kNCopy; j++)
+      s_cb[tid * kNCopy + ((j + tid) & (kNCopy - 1))] = make_uint2(hv[0], hv[1]);
+  }
+
+  constexpr int kTPR = kGemmThreads / BM;
+  constexpr int kCPT = kBKs / kTPR;
+  const int arow = tid / kTPR, acol = (tid % kTPR) * kCPT;
+  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)p.K * 2u;
+  uint32_t a_off = a_bytes;  // past the end: zeros
+  if (r0 + arow < r1) {
+    const int src = (MODE == kModeGateUp && p.row_token) ? p.row_token[r0 + arow] : r0 + arow;
+    a_off = (uint32_t)src * (uint32_t)p.K * 2u;
+  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(MODE == kModeGateUp ? p.x : p.a16, a_bytes);
+  const int nk = p.K / kBKs;
+  const int ng = nk / 4;
+  auto a_kb = [&](int it) { return 256 * (it >> 2) + 32 * (it & 3); };
+
+  // this lane's weight rows: gate/up: block 0 the gate rows, block 1 the up
+  // rows of the same a columns; down: two blocks of 32 outputs
+  constexpr int kWaveCols = MODE == kModeGateUp ? 32 : 64;
+  int wrow[NB];
+  const WView *wv[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    if constexpr (MODE == kModeGateUp) {
+      wrow[nb] = n0 + kWaveCols * wave + l32;
+      wv[nb] = nb == 0 ? &p.w0 : &p.w1;
+    } else {
+      wrow[nb] = n0 + kWaveCols * wave + 32 * nb + l32;
+      wv[nb] = &p.w0;
+    }
+  }
+
+  AStage32<BM> sa[kPA];
+  BRun<FMT, OP> gb0[NB], gb1[NB];
+  BStageBf16x32<OP> sb16[2][NB];
+  auto b16_k = [&](int it) { return 256 * (it >> 2) + 128 * h + 32 * (it & 3); };
+#pragma unroll
+  for (int u = 0; u < kPA; u++) sa[u].load(ra, a_off, a_kb(min(u, nk - 1)), acol);
+  if constexpr (kGroupB) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) gb0[nb].load(*wv[nb], e, wrow[nb], 128 * h);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], b16_k(min(u, nk - 1)));
+  }
+  sa[0].store(&s_a[0][arow * kLdsRowW + acol / 2]);
+  sa[0].load(ra, a_off, a_kb(min(kPA, nk - 1)), acol);
+  __syncthreads();  // A stage 0 and the codebook
+
+  const int m_active = (r1 - r0 + 31) >> 5;  // row blocks holding bucket rows
+  f32x16v_t acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; m++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[m][nb][i] = 0.0f;
+  const uint2 *cb = s_cb + (lane & (kNCopy - 1));
+
+  uint32_t bp[2][NB][16];
+  if constexpr (kGroupB) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) gb0[nb].decode(0, bp[0][nb], cb);
+  }
+
+  auto group = [&](int G, BRun<FMT, OP>(&cur)[NB], BRun<FMT, OP>(&nxt)[NB]) {
+    if constexpr (kGroupB) {
+      const int gn = min(G + 1, ng - 1);
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) nxt[nb].load(*wv[nb], e, wrow[nb], 256 * gn + 128 * h);
+    }
+#pragma unroll
+    for (int S = 0; S < 4; S++) {
+      const int it = 4 * G + S;
+      const uint32_t *A = s_a[it & 1];
+      if constexpr (kGroupB) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          if (S < 3)
+            cur[nb].decode(S + 1, bp[(S + 1) & 1][nb], cb);
+          else
+            nxt[nb].decode(0, bp[(S + 1) & 1][nb], cb);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[S & 1][nb]);
+        const int st = min(it + 2, nk - 1);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], b16_k(st));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        uint4 af[MB];
+#pragma unroll
+        for (int m = 0; m < MB; m++)
+          af[m] = *reinterpret_cast<const uint4 *>(&A[(32 * m + l32) * kLdsRowW + (32 * h + 8 * t) / 2]);
+#pragma unroll
+        for (int m = 0; m < MB; m++) {
+          if (MB > 1 && m >= m_active) continue;
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++) {
+            const uint32_t *b = bp[S & 1][nb];
+            const uint4 bf = make_uint4(b[4 * t], b[4 * t + 1], b[4 * t + 2], b[4 * t + 3]);
+            acc[m][nb] = mfma32<OP>(af[m], bf, acc[m][nb]);
+          }
+        }
+      }
+      const int an = (S + 1) & 3;
+      sa[an].store(&s_a[(it + 1) & 1][arow * kLdsRowW + acol / 2]);
+      sa[an].load(ra, a_off, a_kb(min(it + 1 + kPA, nk - 1)), acol);
+      __syncthreads();
+    }
+  };
+  for (int G = 0; G < ng; G += 2) {
+    group(G, gb0, gb1);
+    if (G + 1 < ng) group(G + 1, gb1, gb0);
+  }
+
+  // result register i of the lane: row 8 (i / 4) + 4 h + i % 4 of the block, column l32
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    if (m >= m_active) continue;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = r0 + 32 * m + 8 * (i / 4) + 4 * h + (i % 4);
+      if (r >= r1) continue;
+      if constexpr (MODE == kModeGateUp) {
+        const float a = silu_mul(acc[m][0][i], acc[m][1][i]);
+        const int col = n0 + kWaveCols * wave + l32;
+        p.a_out[(size_t)r * p.N + (p.a_swap ? swap12(col) : col)] =
+            __builtin_bit_cast(uint16_t, (_Float16)a);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+          p.y_out[(size_t)r * p.N + n0 + kWaveCols * wave + 32 * nb + l32] = acc[m][nb][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dense and skinny (one expert, T <= 64 rows, bf16 weights: the shared expert
 // of a small batch).  Block: 16 output columns; its 8 waves split K, each
 // streaming its share of the 16 (gate/up: 16 + 16) weight rows straight into
@@ -630,13 +969,19 @@ bool gemm_supported(int H, int I, int fmt_gate, int fmt_down) {
 
 namespace {
 
-// grid.x: the layer's output columns over the block's; grid.y: tiles
+// grid.x: the layer's output columns over the block's; grid.y: tiles.  Tiles
+// of 64 and 128 rows run the 32 x 32 x 16 instructions, 16-row tiles the
+// 16 x 16 x 32 ones
 template <int MODE, int BM>
 hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s) {
-#define MOE_GEMM_CASE(F, O)                                                              \
-  if (fmt == F && op == O) {                                                             \
-    return launch(k_gemm<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),      \
-                  dim3(kGemmThreads), s, a);                                             \
+#define MOE_GEMM_CASE(F, O)                                                                  \
+  if (fmt == F && op == O) {                                                                 \
+    if constexpr (BM >= 64)                                                                  \
+      return launch(k_gemm32<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),      \
+                    dim3(kGemmThreads), s, a);                                               \
+    else                                                                                     \
+      return launch(k_gemm<MODE, F, O, BM>, dim3(a.N / block_cols<MODE, F>(), tiles),        \
+                    dim3(kGemmThreads), s, a);                                               \
   }
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpBF16)
   MOE_GEMM_CASE(MOE_FMT_BF16, kOpF16)
