@@ -22,6 +22,8 @@
 // gate/up; fp16 for VQ2 and Q2K gate/up (tokens converted exactly, weights
 // rounded once to fp16) and for every down projection (the SwiGLU output in
 // fp16).  Accumulation in fp32.
+#include <type_traits>
+
 #include "gemv_core.h"
 
 namespace moe {
@@ -647,8 +649,10 @@ struct AStage32 {
   }
 };
 
+// 64-row tiles: two waves per SIMD (the registers capped at 256); 128-row
+// tiles hold 128 accumulators and run one
 template <int MODE, int FMT, int OP, int BM>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm32(GemmArgs p) {
+__global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmArgs p) {
   static_assert(BM == 64 || BM == 128, "32-row blocks");
   constexpr int MB = BM / 32;  // MFMA row blocks
   constexpr int NB = 2;        // 32-column blocks per wave (64 weight rows)
@@ -748,6 +752,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm32(GemmArgs p) {
     for (int nb = 0; nb < NB; nb++) gb0[nb].decode(0, bp[0][nb], cb);
   }
 
+  // MA: row blocks that hold bucket rows, a compile-time constant of the loop
+  // below (a per-block test inside it would cut the loop into branches that
+  // the compiler schedules one by one, each waiting for every LDS read)
+  auto kloop = [&](auto ma_c) {
+  constexpr int MA = decltype(ma_c)::value;
   auto group = [&](int G, BRun<FMT, OP>(&cur)[NB], BRun<FMT, OP>(&nxt)[NB]) {
     if constexpr (kGroupB) {
       const int gn = min(G + 1, ng - 1);
@@ -775,13 +784,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm32(GemmArgs p) {
       }
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        uint4 af[MB];
+        uint4 af[MA];
 #pragma unroll
-        for (int m = 0; m < MB; m++)
+        for (int m = 0; m < MA; m++)
           af[m] = *reinterpret_cast<const uint4 *>(&A[(32 * m + l32) * kLdsRowW + (32 * h + 8 * t) / 2]);
 #pragma unroll
-        for (int m = 0; m < MB; m++) {
-          if (MB > 1 && m >= m_active) continue;
+        for (int m = 0; m < MA; m++) {
 #pragma unroll
           for (int nb = 0; nb < NB; nb++) {
             const uint32_t *b = bp[S & 1][nb];
@@ -799,6 +807,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm32(GemmArgs p) {
   for (int G = 0; G < ng; G += 2) {
     group(G, gb0, gb1);
     if (G + 1 < ng) group(G + 1, gb1, gb0);
+  }
+  };
+  // 64-row tiles: one or both 32-row blocks; 128-row tiles (one dense expert,
+  // all tiles full but the last) always all four
+  if constexpr (MB == 2) {
+    if (m_active >= 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  } else {
+    kloop(std::integral_constant<int, MB>{});
   }
 
   // result register i of the lane: row 8 (i / 4) + 4 h + i % 4 of the block, column l32
