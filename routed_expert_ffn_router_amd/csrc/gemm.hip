@@ -658,7 +658,9 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
   constexpr int NB = 2;        // 32-column blocks per wave (64 weight rows)
   constexpr int kPA = 4;       // A stages in flight (one group)
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
-  __shared__ uint32_t s_a[2][BM * kLdsRowW];
+  // A stages in LDS: a ring of four, each stage written two stages before it
+  // is read, so that one barrier serves two stages
+  __shared__ uint32_t s_a[4][BM * kLdsRowW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   // XCD-aware order, as in k_gemm
   const uint32_t nbx = gridDim.x, nby = gridDim.y;
@@ -732,9 +734,12 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], b16_k(min(u, nk - 1)));
   }
-  sa[0].store(&s_a[0][arow * kLdsRowW + acol / 2]);
-  sa[0].load(ra, a_off, a_kb(min(kPA, nk - 1)), acol);
-  __syncthreads();  // A stage 0 and the codebook
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    sa[u].store(&s_a[u][arow * kLdsRowW + acol / 2]);
+    sa[u].load(ra, a_off, a_kb(min(kPA + u, nk - 1)), acol);
+  }
+  __syncthreads();  // A stages 0 and 1 and the codebook
 
   const int m_active = (r1 - r0 + 31) >> 5;  // row blocks holding bucket rows
   f32x16v_t acc[MB][NB];
@@ -746,8 +751,14 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
       for (int i = 0; i < 16; i++) acc[m][nb][i] = 0.0f;
   const uint2 *cb = s_cb + (lane & (kNCopy - 1));
 
-  uint32_t bp[2][NB][16];
-  if constexpr (kGroupB) {
+  // B operands: VQ2 and Q2K decode one stage ahead into the other buffer of
+  // bp (their decode is long enough to be worth overlapping); MXFP4 and bf16
+  // weights convert in a few instructions, so they decode each stage just
+  // before its matrix instructions into one buffer, which keeps the 64-row
+  // tiles within 256 registers
+  constexpr bool kJit = FMT == MOE_FMT_MXFP4 || FMT == MOE_FMT_BF16;
+  uint32_t bp[kJit ? 1 : 2][NB][16];
+  if constexpr (kGroupB && !kJit) {
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) gb0[nb].decode(0, bp[0][nb], cb);
   }
@@ -766,8 +777,12 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 #pragma unroll
     for (int S = 0; S < 4; S++) {
       const int it = 4 * G + S;
-      const uint32_t *A = s_a[it & 1];
-      if constexpr (kGroupB) {
+      const uint32_t *A = s_a[it & 3];
+      const int kCur = kJit ? 0 : (S & 1);  // bp buffer this stage reads
+      if constexpr (kGroupB && kJit) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) cur[nb].decode(S, bp[0][nb], cb);
+      } else if constexpr (kGroupB) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
           if (S < 3)
@@ -777,7 +792,7 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[S & 1][nb]);
+        for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].decode(bp[0][nb]);
         const int st = min(it + 2, nk - 1);
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) sb16[S & 1][nb].load(*wv[nb], e, wrow[nb], b16_k(st));
@@ -792,16 +807,18 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
         for (int m = 0; m < MA; m++) {
 #pragma unroll
           for (int nb = 0; nb < NB; nb++) {
-            const uint32_t *b = bp[S & 1][nb];
+            const uint32_t *b = bp[kCur][nb];
             const uint4 bf = make_uint4(b[4 * t], b[4 * t + 1], b[4 * t + 2], b[4 * t + 3]);
             acc[m][nb] = mfma32<OP>(af[m], bf, acc[m][nb]);
           }
         }
       }
-      const int an = (S + 1) & 3;
-      sa[an].store(&s_a[(it + 1) & 1][arow * kLdsRowW + acol / 2]);
-      sa[an].load(ra, a_off, a_kb(min(it + 1 + kPA, nk - 1)), acol);
-      __syncthreads();
+      // stage it + 2 into the buffer stage it - 2 read (every wave left it
+      // before the last barrier); stage it + 2 + kPA into its registers
+      const int an = (S + 2) & 3;
+      sa[an].store(&s_a[(it + 2) & 3][arow * kLdsRowW + acol / 2]);
+      sa[an].load(ra, a_off, a_kb(min(it + 2 + kPA, nk - 1)), acol);
+      if (S & 1) __syncthreads();
     }
   };
   for (int G = 0; G < ng; G += 2) {
