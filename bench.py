@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -71,13 +72,16 @@ def _args():
 # HBM traffic from hardware counters
 # --------------------------------------------------------------------------
 
-# marker name -> substring of the HIP kernel's symbol
-KERNEL_OF = {"decode_p1": "k_dec_p1", "decode_p2": "k_dec_p2", "decode_p3": "k_dec_p3",
-             "router": "k_router", "gemm_gateup": "k_gemm<0, 2", "gemm_down": "k_gemm<1, 1",
-             "combine": "k_combine", "select": "k_select", "select_plan": "k_select_plan",
-             "routed_gateup": "k_gateup", "routed_down": "k_down", "shared_gateup": "k_gateup",
-             "shared_down": "k_down", "a8_gemm_gateup": "k_gemm_a8<0", "a8_gemm_down": "k_gemm_a8<1",
-             "act_quant": "k_mx8_quant", "tokens_f16": "k_tokens_f16"}
+# marker name -> pattern (re.search) of the HIP kernel's symbol; the grouped
+# GEMM markers take the routed weight formats only (Q2K, VQ2, MXFP4: template
+# argument 1, 2 or 3), not the shared expert's bf16 instance
+KERNEL_OF = {"decode_p1": r"k_dec_p1<", "decode_p2": r"k_dec_p2<", "decode_p3": r"k_dec_p3<",
+             "router": r"k_router", "gemm_gateup": r"k_gemm(32)?<0, [123],",
+             "gemm_down": r"k_gemm(32)?<1, [123],", "combine": r"k_combine\b",
+             "select": r"k_select\(", "select_plan": r"k_select_plan", "routed_gateup": r"k_gateup",
+             "routed_down": r"k_down", "shared_gateup": r"k_gateup", "shared_down": r"k_down",
+             "a8_gemm_gateup": r"k_gemm_a8<0", "a8_gemm_down": r"k_gemm_a8<1",
+             "act_quant": r"k_mx8_quant", "tokens_f16": r"k_tokens_f16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -171,7 +175,7 @@ def measured_traffic(workload, marker):
         rec = json.load(fh).get(workload)
     if not rec:
         return None
-    hits = [(k, v) for k, v in rec["kernels"].items() if KERNEL_OF[marker] in k]
+    hits = [(k, v) for k, v in rec["kernels"].items() if re.search(KERNEL_OF[marker], k)]
     if len(hits) != 1 or hits[0][1].get("sources_sha") != sources_sha(hits[0][0]):
         return None
     return hits[0][1]["bytes"]
