@@ -743,7 +743,7 @@ static int cache_planes(const moe_weights &host, const moe_weights &slot, CacheS
                   "aligned", per[i]);
     void *dev = nullptr;
     MOE_TRY(hip_check(hipHostGetDevicePointer(&dev, const_cast<void *>(planes[i]), 0),
-                      "cache: host weights must come from hipHostMalloc"));
+                      "cache: host weights must be pinned, device-mapped host memory"));
     cs.src[cs.n_planes] = static_cast<const uint8_t *>(dev);
     cs.dst[cs.n_planes] = static_cast<uint8_t *>(dplanes[i]);
     cs.per_bytes[cs.n_planes] = per[i];
