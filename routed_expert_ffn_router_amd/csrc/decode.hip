@@ -202,9 +202,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))
   // every routed row pair's loads go out at once (MXFP4's larger chunks: two)
   constexpr int kRPF = RFMT == MOE_FMT_MXFP4 ? 2 : ST;
   gateup_rows<RFMT, RSPL, 64, ST, 1, kRPF, kCopies>(p.gate, p.up, p.H, p.I, p.x, e_sel, j, j + 1,
-                                                    nullptr, 0, p.a, row_base,
-                                                    s_cb + (lane % kCopies), p.a_mode, p.a_hi,
-                                                    p.a_lo);
+                                                    nullptr, 0, p.a, row_base, s_cb, p.a_mode,
+                                                    p.a_hi, p.a_lo);
 }
 
 // ---------------------------------------------------------------------------

@@ -386,10 +386,15 @@ struct Chunk<MOE_FMT_VQ2, SPL, LPR> {
       d[i] = buf_u16(rs, vs + (k / 256) * 2, ss);
     }
   }
-  // cb: this lane's codebook copy in LDS (entry e at cb[e * NC], NC copies)
+  // cb: this lane's codebook copy in LDS (entry e at cb[e * NC], NC copies);
+  // with NC == 32 the table itself (entry e, copy c at byte 256 e + 8 c) and
+  // each lane reads copy lane % 32: the byte offset of code byte b is then
+  // (byte << 8) | 8 (lane % 32), which one v_perm_b32 assembles (byte 1 from
+  // the code word, byte 0 from the lane's copy offset, zeros above)
   template <int NT, int NC = kNCopy>
   __device__ __forceinline__ void dot_x(const uint32_t (&xw)[NT][SPL][8], const uint2 *cb,
                                         float (&out)[NT]) const {
+    const uint32_t lane_off = (threadIdx.x & 31u) << 3;
 #pragma unroll
     for (int t = 0; t < NT; t++) out[t] = 0.0f;
 #pragma unroll
@@ -399,7 +404,14 @@ struct Chunk<MOE_FMT_VQ2, SPL, LPR> {
       for (int t = 0; t < NT; t++) acc[t] = 0.0f;
 #pragma unroll
       for (int b = 0; b < 4; b++) {
-        const uint2 c = cb[((code[i] >> (8 * b)) & 255u) * NC];
+        uint2 c;
+        if constexpr (NC == 32) {
+          const uint32_t off =
+              __builtin_amdgcn_perm(code[i], lane_off, 0x0C0C0000u | ((4u + b) << 8));
+          c = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(cb) + off);
+        } else {
+          c = cb[((code[i] >> (8 * b)) & 255u) * NC];
+        }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
           acc[t] = dot2_bf16(xw[t][i][2 * b], c.x, acc[t]);
