@@ -557,9 +557,14 @@ struct BRun {
     if constexpr (FMT == MOE_FMT_VQ2) {
       const f16x2_t d2 = {__builtin_bit_cast(_Float16, (uint16_t)s0),
                           __builtin_bit_cast(_Float16, (uint16_t)s0)};
+      // cb: the table, entry e and copy c at byte 256 e + 8 c (32 copies);
+      // lane l reads copy l % 32 at (code byte << 8) | 8 (l % 32), one v_perm_b32
+      const uint32_t lane_off = (threadIdx.x & 31u) << 3;
 #pragma unroll
       for (int c = 0; c < 8; c++) {
-        const uint2 v = cb[((q[2 * S + c / 4] >> (8 * (c % 4))) & 255u) * kNCopy];
+        const uint32_t off = __builtin_amdgcn_perm(q[2 * S + c / 4], lane_off,
+                                                   0x0C0C0000u | ((4u + (c % 4)) << 8));
+        const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(cb) + off);
         out[2 * c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * d2);
         out[2 * c + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * d2);
       }
@@ -647,6 +652,14 @@ struct AStage32 {
     for (int i = 0; i < kCPT / 8; i++)
       d4[i] = make_uint4(raw[4 * i], raw[4 * i + 1], raw[4 * i + 2], raw[4 * i + 3]);
   }
+  // into an unpadded 128-byte row whose 16-byte chunks are XOR-swizzled by
+  // sw: chunk c of the row sits at chunk c ^ sw
+  __device__ __forceinline__ void store_sw(uint32_t *row, int c0, int sw) const {
+#pragma unroll
+    for (int i = 0; i < kCPT / 8; i++)
+      *reinterpret_cast<uint4 *>(row + 4 * ((c0 + i) ^ sw)) =
+          make_uint4(raw[4 * i], raw[4 * i + 1], raw[4 * i + 2], raw[4 * i + 3]);
+  }
 };
 
 // 64-row tiles: two waves per SIMD (the registers capped at 256); 128-row
@@ -658,10 +671,19 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
   constexpr int NB = 2;        // 32-column blocks per wave (64 weight rows)
   constexpr int kPA = 4;       // A stages in flight (one group)
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
-  // A stages in LDS: a ring of four, each stage written two stages before it
-  // is read, so that one barrier serves two stages
-  __shared__ uint32_t s_a[4][BM * kLdsRowW];
-  __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
+  // A stages in LDS.  VQ2: two unpadded 128-byte rows per stage buffer, 16-byte
+  // chunks XOR-swizzled by (row / 2) % 8 (a 16-lane group of operand reads
+  // then covers all 64 banks), so that the 64 KB codebook of 32 copies fits
+  // beside them in two blocks per CU; one barrier per stage.  Other formats:
+  // a ring of four padded buffers, each stage written two stages before it
+  // is read, one barrier per two stages.
+  constexpr bool kSw = FMT == MOE_FMT_VQ2;
+  constexpr int kNBuf = kSw ? 2 : 4;
+  constexpr int kLead = kNBuf / 2;  // stages between an A stage's store and its read
+  constexpr int kAW = kSw ? kBKs / 2 : kLdsRowW;  // dwords per staged row
+  constexpr int kCbCopies = 32;
+  __shared__ uint32_t s_a[kNBuf][BM * kAW];
+  __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kCbCopies : 1];
   // XCD-aware order, as in k_gemm
   const uint32_t nbx = gridDim.x, nby = gridDim.y;
   const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
@@ -677,7 +699,7 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
   const int l32 = lane & 31, h = lane >> 5;  // MFMA row / column within a block; k half
   const int n0 = bx * block_cols<MODE, FMT>();
 
-  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, kNCopy copies
+  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, kCbCopies copies
     const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[tid];
     uint32_t hv[2];
 #pragma unroll
@@ -685,8 +707,8 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
       hv[j] = pack_h2((float)(int)(int8_t)((cw >> (16 * j)) & 255u),
                       (float)(int)(int8_t)((cw >> (16 * j + 8)) & 255u));
 #pragma unroll
-    for (int j = 0; j < kNCopy; j++)
-      s_cb[tid * kNCopy + ((j + tid) & (kNCopy - 1))] = make_uint2(hv[0], hv[1]);
+    for (int j = 0; j < kCbCopies; j++)
+      s_cb[tid * kCbCopies + ((j + tid) & (kCbCopies - 1))] = make_uint2(hv[0], hv[1]);
   }
 
   constexpr int kTPR = kGemmThreads / BM;
@@ -734,12 +756,18 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], b16_k(min(u, nk - 1)));
   }
+  auto a_store = [&](const AStage32<BM> &st, int buf) {
+    if constexpr (kSw)
+      st.store_sw(&s_a[buf][arow * kAW], acol / 8, (arow >> 1) & 7);
+    else
+      st.store(&s_a[buf][arow * kAW + acol / 2]);
+  };
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    sa[u].store(&s_a[u][arow * kLdsRowW + acol / 2]);
+  for (int u = 0; u < kLead; u++) {
+    a_store(sa[u], u);
     sa[u].load(ra, a_off, a_kb(min(kPA + u, nk - 1)), acol);
   }
-  __syncthreads();  // A stages 0 and 1 and the codebook
+  __syncthreads();  // the first A stages and the codebook
 
   const int m_active = (r1 - r0 + 31) >> 5;  // row blocks holding bucket rows
   f32x16v_t acc[MB][NB];
@@ -749,7 +777,7 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) acc[m][nb][i] = 0.0f;
-  const uint2 *cb = s_cb + (lane & (kNCopy - 1));
+  const uint2 *cb = s_cb;
 
   // B operands: VQ2 and Q2K decode one stage ahead into the other buffer of
   // bp (their decode is long enough to be worth overlapping); MXFP4 and bf16
@@ -777,7 +805,7 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 #pragma unroll
     for (int S = 0; S < 4; S++) {
       const int it = 4 * G + S;
-      const uint32_t *A = s_a[it & 3];
+      const uint32_t *A = s_a[it % kNBuf];
       const int kCur = kJit ? 0 : (S & 1);  // bp buffer this stage reads
       if constexpr (kGroupB && kJit) {
 #pragma unroll
@@ -801,8 +829,13 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
       for (int t = 0; t < 4; t++) {
         uint4 af[MA];
 #pragma unroll
-        for (int m = 0; m < MA; m++)
-          af[m] = *reinterpret_cast<const uint4 *>(&A[(32 * m + l32) * kLdsRowW + (32 * h + 8 * t) / 2]);
+        for (int m = 0; m < MA; m++) {
+          if constexpr (kSw)
+            af[m] = *reinterpret_cast<const uint4 *>(
+                &A[(32 * m + l32) * kAW + 4 * ((4 * h + t) ^ ((l32 >> 1) & 7))]);
+          else
+            af[m] = *reinterpret_cast<const uint4 *>(&A[(32 * m + l32) * kAW + (32 * h + 8 * t) / 2]);
+        }
 #pragma unroll
         for (int m = 0; m < MA; m++) {
 #pragma unroll
@@ -813,12 +846,13 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
           }
         }
       }
-      // stage it + 2 into the buffer stage it - 2 read (every wave left it
-      // before the last barrier); stage it + 2 + kPA into its registers
-      const int an = (S + 2) & 3;
-      sa[an].store(&s_a[(it + 2) & 3][arow * kLdsRowW + acol / 2]);
-      sa[an].load(ra, a_off, a_kb(min(it + 2 + kPA, nk - 1)), acol);
-      if (S & 1) __syncthreads();
+      // stage it + kLead into the buffer that stage it - kLead read (every
+      // wave left it before the last barrier); stage it + kLead + kPA into
+      // its registers
+      const int an = (S + kLead) & 3;
+      a_store(sa[an], (it + kLead) % kNBuf);
+      sa[an].load(ra, a_off, a_kb(min(it + kLead + kPA, nk - 1)), acol);
+      if (S % kLead == kLead - 1) __syncthreads();
     }
   };
   for (int G = 0; G < ng; G += 2) {
