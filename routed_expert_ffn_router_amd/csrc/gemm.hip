@@ -919,6 +919,198 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 }
 
 // ---------------------------------------------------------------------------
+// One dense bf16 expert over all T rows (the shared expert from 96 tokens),
+// with both operands staged in LDS by direct loads.  A block computes 128
+// rows against 256 weight rows: gate/up takes 128 gate and the 128 up rows of
+// the same SwiGLU columns (wave w: columns 32 w + [0, 32) of both), down 256
+// outputs (wave w: outputs 64 w + [0, 64)); every wave covers all 128 rows
+// (4 x 2 accumulators of 32 x 32).  buffer_load_dwordx4 ... lds moves 16
+// bytes per lane from global memory into LDS (lane i of a wave's load writes
+// slot i of a 1 KB run, from whatever global address the lane names), three
+// K stages of 64 deep, so no register holds a staged tile and the matrix
+// instructions of one wave per SIMD have a whole stage of loads ahead of
+// them.  LDS rows are 128 bytes, unpadded, 16-byte chunks XOR-swizzled by
+// (row / 2) % 8 (a 16-lane group of operand reads covers all 64 banks).
+// Reduction slots: instruction t of a stage takes chunks 2t (lane half 0)
+// and 2t + 1 (half 1) of every row, for A and B alike.  Gate/up multiplies
+// bf16 tokens by bf16 weights and writes the fp16 SwiGLU output; down
+// multiplies that fp16 output by the weights converted to fp16 as they leave
+// LDS (exact in the binary16 range) and writes fp32.
+// ---------------------------------------------------------------------------
+constexpr int kDnRows = 128;   // rows per block
+constexpr int kDnB = 256;      // weight rows per block
+constexpr int kDnK = 64;       // K per stage
+constexpr int kDnStages = 3;   // stages in LDS
+
+template <int MODE>
+constexpr int dense_cols() { return MODE == kModeGateUp ? kDnB / 2 : kDnB; }
+
+struct DenseArgs {
+  int T, K, N;             // rows, reduction length, output columns
+  const uint16_t *a;       // gate/up: bf16 tokens [T][K]; down: fp16 SwiGLU output [T][K]
+  const uint16_t *w0, *w1;  // bf16 [N][K]: gate and up, or down (w1 unused)
+  uint16_t *a_out;         // gate/up: fp16 [T][N]
+  float *y_out;            // down: fp32 [T][N]
+  int a_swap;              // gate/up: a_out in Q2K slot order
+};
+
+typedef int i32x4r_t __attribute__((ext_vector_type(4)));
+// buffer resource words for a byte range (as make_rsrc), for the asm below
+__device__ __forceinline__ i32x4r_t rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return (i32x4r_t){(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes,
+                    (int)kBufDword3};
+}
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+// 16 bytes per lane from global memory (buffer offset vo) into LDS: lane i of
+// the wave writes bytes 16 i .. 16 i + 15 after lds (a wave-uniform LDS byte
+// address).  Written as asm so that the compiler, which cannot tell which LDS
+// buffer such a load writes, does not make every later LDS read wait for it;
+// the kernel waits for these loads itself (vmcnt) before the barrier that
+// publishes them.  No register result: nothing is written to registers.
+__device__ __forceinline__ void lds_load16(i32x4r_t r, uint32_t lds, uint32_t vo) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(vo), "s"(r)
+               : "memory", "m0");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
+  constexpr int kRowU = kDnK / 2;  // dwords per staged row
+  constexpr int OP = MODE == kModeGateUp ? kOpBF16 : kOpF16;
+  __shared__ __attribute__((aligned(16))) uint32_t s_a[kDnStages][kDnRows * kRowU];
+  __shared__ __attribute__((aligned(16))) uint32_t s_b[kDnStages][kDnB * kRowU];
+  // weights-first block order, XCD-aware (as the grouped GEMM's dense case)
+  const uint32_t nbx = gridDim.x, nby = gridDim.y;
+  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t jx = bid >> 3;
+  const int ti = (int)(jx % nby), bx = (int)((jx / nby) * 8 + (bid & 7));
+  const int row0 = ti * kDnRows, n0 = bx * dense_cols<MODE>();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int nk = p.K / kDnK;
+
+  // this lane's slot in each of the wave's direct loads: run j of a stage
+  // holds rows 8 j .. 8 j + 7; lane i writes slot i: row 8 j + i / 8, physical
+  // chunk i % 8, which holds logical chunk (i % 8) ^ ((row / 2) % 8)
+  const i32x4r_t ra = rsrc_words(p.a, (uint32_t)p.T * (uint32_t)p.K * 2u);
+  const uint32_t wb = (uint32_t)p.N * (uint32_t)p.K * 2u;
+  const i32x4r_t r0 = rsrc_words(p.w0, wb), r1 = rsrc_words(MODE == kModeGateUp ? p.w1 : p.w0, wb);
+  constexpr int kARuns = kDnRows / 8 / 4;  // A runs per wave and stage: 4
+  constexpr int kBRuns = kDnB / 8 / 4;     // B runs per wave and stage: 8
+  uint32_t avo[kARuns], bvo[kBRuns];
+#pragma unroll
+  for (int u = 0; u < kARuns; u++) {
+    const int j = kARuns * wave + u, row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int gr = min(row0 + row, p.T - 1);  // rows past T repeat row T - 1 (not stored)
+    avo[u] = ((uint32_t)gr * (uint32_t)p.K + 8u * (uint32_t)c) * 2u;
+  }
+#pragma unroll
+  for (int u = 0; u < kBRuns; u++) {
+    const int j = kBRuns * wave + u, row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    // gate/up: rows below 128 are gate rows n0 + row, the rest up rows
+    const int wr = n0 + (MODE == kModeGateUp ? (row & (kDnB / 2 - 1)) : row);
+    bvo[u] = ((uint32_t)wr * (uint32_t)p.K + 8u * (uint32_t)c) * 2u;
+  }
+  auto issue = [&](int it) {
+    const int buf = it % kDnStages;
+    const uint32_t ko = (uint32_t)it * kDnK * 2u;
+#pragma unroll
+    for (int u = 0; u < kARuns; u++)
+      lds_load16(ra, lds_offset(&s_a[buf][(kARuns * wave + u) * 256]), avo[u] + ko);
+#pragma unroll
+    for (int u = 0; u < kBRuns; u++) {
+      const int j = kBRuns * wave + u;
+      lds_load16(MODE == kModeGateUp && j >= kDnB / 16 ? r1 : r0, lds_offset(&s_b[buf][j * 256]),
+                 bvo[u] + ko);
+    }
+  };
+
+  f32x16v_t acc[4][2];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int nb = 0; nb < 2; nb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[m][nb][i] = 0.0f;
+
+  issue(0);
+  if (nk > 1) issue(1);
+  // stage 0 in LDS for every wave (this wave's stage-1 loads may still fly)
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt <= 12
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+  __syncthreads();
+  for (int it = 0; it < nk; it++) {
+    if (it + 2 < nk) issue(it + 2);
+    const uint32_t *A = s_a[it % kDnStages];
+    const uint32_t *B = s_b[it % kDnStages];
+    auto a_frag = [&](int m, int t) {
+      const int row = 32 * m + l32;
+      return *reinterpret_cast<const uint4 *>(&A[row * kRowU + 4 * ((2 * t + h) ^ ((row >> 1) & 7))]);
+    };
+    auto b_frag = [&](int nb, int t) {
+      const int row = MODE == kModeGateUp ? (kDnB / 2) * nb + 32 * wave + l32 : 64 * wave + 32 * nb + l32;
+      const uint4 v =
+          *reinterpret_cast<const uint4 *>(&B[row * kRowU + 4 * ((2 * t + h) ^ ((row >> 1) & 7))]);
+      if constexpr (MODE == kModeGateUp)
+        return v;
+      else
+        return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+                          bf16x2_to_f16x2(v.w));
+    };
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      uint4 bf[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; nb++) bf[nb] = b_frag(nb, t);
+#pragma unroll
+      for (int m = 0; m < 4; m++) {
+        const uint4 af = a_frag(m, t);
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++) acc[m][nb] = mfma32<OP>(af, bf[nb], acc[m][nb]);
+      }
+    }
+    if (it + 1 < nk) {
+      // stage it + 1 complete for this wave (stage it + 2's loads may fly),
+      // then for every wave; the barrier also ends this stage's reads of the
+      // buffer that stage it + 3 overwrites
+      if (it + 2 < nk)
+        __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt <= 12
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+      __syncthreads();
+    }
+  }
+
+  // result register i: row 8 (i / 4) + 4 h + i % 4 of row block m, column l32
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = row0 + 32 * m + 8 * (i / 4) + 4 * h + (i % 4);
+      if (r >= p.T) continue;
+      if constexpr (MODE == kModeGateUp) {
+        const float a = silu_mul(acc[m][0][i], acc[m][1][i]);
+        const int col = n0 + 32 * wave + l32;
+        p.a_out[(size_t)r * p.N + (p.a_swap ? swap12(col) : col)] =
+            __builtin_bit_cast(uint16_t, (_Float16)a);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++) p.y_out[(size_t)r * p.N + n0 + 64 * wave + 32 * nb + l32] = acc[m][nb][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dense and skinny (one expert, T <= 64 rows, bf16 weights: the shared expert
 // of a small batch).  Block: 16 output columns; its 8 waves split K, each
 // streaming its share of the 16 (gate/up: 16 + 16) weight rows straight into
@@ -1125,7 +1317,20 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   // one dense expert with many row tiles: keep each weight block in an L2
   g.weight_major = !offsets && (I / block_cols<kModeGateUp, MOE_FMT_BF16>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
-  err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s);
+  // one dense bf16 expert from 128-row tiles: both operands staged in LDS by
+  // direct loads (the column blocks a multiple of 8 for the block order)
+  const bool dense = BM == 128 && !offsets && gate.fmt == MOE_FMT_BF16 &&
+                     down.fmt == MOE_FMT_BF16 && H % kDnK == 0 && I % kDnK == 0 &&
+                     I % (8 * dense_cols<kModeGateUp>()) == 0 &&
+                     H % (8 * dense_cols<kModeDown>()) == 0;
+  if (dense) {
+    DenseArgs da{T, H, I, x, reinterpret_cast<const uint16_t *>(gate.data),
+                 reinterpret_cast<const uint16_t *>(up.data), a16, nullptr, g.a_swap};
+    err = launch(k_dense<kModeGateUp>, dim3(I / dense_cols<kModeGateUp>(), (T + kDnRows - 1) / kDnRows),
+                 dim3(kGemmThreads), s, da);
+  } else {
+    err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s);
+  }
   if (err != hipSuccess) return err;
 
   GemmArgs d{};
@@ -1133,6 +1338,12 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
   d.weight_major = !offsets && (H / block_cols<kModeDown, MOE_FMT_BF16>()) % 8 == 0 && max_tiles >= 16;
   d.y_out = y;
   if (mark) mark(mark_ctx, names[2]);
+  if (dense) {
+    DenseArgs dd{n_rows, I, H, a16, reinterpret_cast<const uint16_t *>(down.data), nullptr,
+                 nullptr, y, 0};
+    return launch(k_dense<kModeDown>, dim3(H / dense_cols<kModeDown>(), (n_rows + kDnRows - 1) / kDnRows),
+                  dim3(kGemmThreads), s, dd);
+  }
   return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, max_tiles, s);
 }
 
