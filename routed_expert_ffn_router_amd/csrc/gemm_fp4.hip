@@ -168,7 +168,13 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
   };
   auto a_load = [&](AStg &st, int it) {
     const uint32_t ko = (uint32_t)it * kA8K;
-    if constexpr (kBPT == 32) {
+    if constexpr (kBPT == 64) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const u32x4_t x = buf_u128(ra, a_off + ko + 16 * q, 0);
+        st.v[4 * q] = x.x, st.v[4 * q + 1] = x.y, st.v[4 * q + 2] = x.z, st.v[4 * q + 3] = x.w;
+      }
+    } else if constexpr (kBPT == 32) {
       const u32x4_t x0 = buf_u128(ra, a_off + ko, 0), x1 = buf_u128(ra, a_off + ko + 16, 0);
       st.v[0] = x0.x, st.v[1] = x0.y, st.v[2] = x0.z, st.v[3] = x0.w;
       st.v[4] = x1.x, st.v[5] = x1.y, st.v[6] = x1.z, st.v[7] = x1.w;
@@ -180,7 +186,12 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
   };
   auto a_store = [&](const AStg &st, int buf) {
     uint8_t *dst = &s_a[buf][arow * kA8Row + acol];
-    if constexpr (kBPT == 32) {
+    if constexpr (kBPT == 64) {
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        *reinterpret_cast<uint4 *>(dst + 16 * q) =
+            make_uint4(st.v[4 * q], st.v[4 * q + 1], st.v[4 * q + 2], st.v[4 * q + 3]);
+    } else if constexpr (kBPT == 32) {
       *reinterpret_cast<uint4 *>(dst) = make_uint4(st.v[0], st.v[1], st.v[2], st.v[3]);
       *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(st.v[4], st.v[5], st.v[6], st.v[7]);
     } else {
@@ -401,6 +412,11 @@ hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, 
       launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, T, H, x, xq, xs);
   if (err != hipSuccess) return err;
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
+  // 128-row tiles from 96 rows per active expert: each expert's weights then
+  // stream about once per bucket rather than once per 64 rows
+  if (n_rows >= 96 * active)
+    return a8_bm<128>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq,
+                      as, a_trace, y, s, mark, mark_ctx, names);
   if (n_rows >= 32 * active)
     return a8_bm<64>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq,
                      as, a_trace, y, s, mark, mark_ctx, names);
