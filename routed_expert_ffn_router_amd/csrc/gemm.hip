@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "gemv_core.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -954,29 +955,6 @@ struct DenseArgs {
   int a_swap;              // gate/up: a_out in Q2K slot order
 };
 
-typedef int i32x4r_t __attribute__((ext_vector_type(4)));
-// buffer resource words for a byte range (as make_rsrc), for the asm below
-__device__ __forceinline__ i32x4r_t rsrc_words(const void *base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return (i32x4r_t){(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes,
-                    (int)kBufDword3};
-}
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
-}
-// 16 bytes per lane from global memory (buffer offset vo) into LDS: lane i of
-// the wave writes bytes 16 i .. 16 i + 15 after lds (a wave-uniform LDS byte
-// address).  Written as asm so that the compiler, which cannot tell which LDS
-// buffer such a load writes, does not make every later LDS read wait for it;
-// the kernel waits for these loads itself (vmcnt) before the barrier that
-// publishes them.  No register result: nothing is written to registers.
-__device__ __forceinline__ void lds_load16(i32x4r_t r, uint32_t lds, uint32_t vo) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(vo), "s"(r)
-               : "memory", "m0");
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
   constexpr int kRowU = kDnK / 2;  // dwords per staged row
@@ -1044,9 +1022,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
   if (nk > 1) issue(1);
   // stage 0 in LDS for every wave (this wave's stage-1 loads may still fly)
   if (nk > 1)
-    __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt <= 12
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
   else
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   for (int it = 0; it < nk; it++) {
     if (it + 2 < nk) issue(it + 2);
@@ -1083,9 +1061,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
       // then for every wave; the barrier also ends this stage's reads of the
       // buffer that stage it + 3 overwrites
       if (it + 2 < nk)
-        __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt <= 12
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
       else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __syncthreads();
     }
   }

@@ -28,7 +28,10 @@
 // step of 128, the weight bytes go straight from memory into the operand
 // registers.  Gate/up's epilogue applies SwiGLU and quantizes the result to
 // MX-FP8 (a wave's 32 columns of a row are exactly one scale group).
+#include <type_traits>
+
 #include "gemv_core.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -331,6 +334,217 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
 }
 
 // ---------------------------------------------------------------------------
+// 128-row tiles with every operand moved into LDS by direct loads (as the
+// dense bf16 GEMM).  A block of 8 waves computes 128 bucket rows of one expert
+// against 256 weight rows: wave (h, c) = (w / 4, w % 4) takes rows 64 h +
+// [0, 64) and the columns of k_gemm_a8's wave c (gate/up: columns 32 c +
+// [0, 32) of gate and of up, one MX-FP8 scale group; down: outputs 64 c +
+// [0, 64)), 4 x 4 accumulators of 16 x 16, which stay in VGPRs at two waves
+// per SIMD.  Each weight byte is staged once per 128 rows.  Three K stages of
+// 128 in LDS:
+//   A codes, 128 rows x 128 bytes, 16-byte chunks XOR-swizzled by
+//     (row / 2) % 8; the MFMA's A lane (row r, lane group g) reads chunks g
+//     and 4 + g of its row;
+//   B nibbles, 256 rows x 64 bytes stored chunk-major (chunk g of every row,
+//     then chunk g + 1), so the 16 lanes of a lane group read consecutive
+//     16-byte slots; B lane (column n, group g) reads chunk g of row n;
+//   the E8M0 scale dwords of A and B rows (4 k-blocks of 32 per stage).
+// Every wave issues the same 5 direct loads per stage: 2 runs of A, 2 runs of
+// B and one scale load (waves 0-3: 32 A rows each; waves 4-7: 64 B rows).
+// The loop is compiled once per count of live 16-row blocks of the wave's
+// half (0, 2 or 4; a wave with none still loads and keeps the barriers).
+// ---------------------------------------------------------------------------
+constexpr int kA8DmaThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
+  constexpr int BM = 128, NB = 4, kStg = 3, kWB = 256;
+  constexpr int kAB = kA8K, kBB = kA8K / 2;  // A and B bytes per row and stage
+  constexpr int kDma = 5;                    // direct loads per wave and stage
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[kStg][BM * kAB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[kStg][kWB * kBB];
+  __shared__ __attribute__((aligned(16))) uint32_t s_as[kStg][BM];
+  __shared__ __attribute__((aligned(16))) uint32_t s_bs[kStg][kWB];
+
+  const uint32_t nbx = gridDim.x, nby = gridDim.y;
+  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t jx = bid >> 3;
+  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
+  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
+  if (ti >= p.tiles[0]) return;
+  const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
+  const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
+  const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wh = wave >> 2, wc = wave & 3;  // row half, column group
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = bx * a8_block_cols<MODE>();
+  const int nk = p.K / kA8K;
+  const uint32_t ks = (uint32_t)(p.K / 32);  // scale bytes per row
+
+  // A: the source row of bucket row r (rows past the bucket repeat its last
+  // row; their results are not stored)
+  auto a_src = [&](int row) {
+    const int r = min(r0 + row, r1 - 1);
+    return p.row_token ? p.row_token[r] : r;
+  };
+  const i32x4r_t ra = rsrc_words(p.aq, (uint32_t)p.a_rows * (uint32_t)p.K);
+  const i32x4r_t ras = rsrc_words(p.as, (uint32_t)p.a_rows * ks);
+  const uint32_t db = (uint32_t)expert_data_bytes(MOE_FMT_MXFP4, p.w0.N, p.w0.K);
+  const uint32_t sb = (uint32_t)expert_scale_bytes(MOE_FMT_MXFP4, p.w0.N, p.w0.K);
+  const i32x4r_t rb0 = rsrc_words(p.w0.data + (size_t)e * db, db);
+  const i32x4r_t rb1 = rsrc_words(p.w1.data + (size_t)e * db, db);
+  const i32x4r_t rs0 = rsrc_words(p.w0.scales + (size_t)e * sb, sb);
+  const i32x4r_t rs1 = rsrc_words(p.w1.scales + (size_t)e * sb, sb);
+  // weight row of LDS B row b (gate/up: rows below 128 gate, the rest up)
+  auto w_row = [&](int b) { return n0 + (MODE == kModeGateUp ? (b & 127) : b); };
+
+  // A runs 2w, 2w + 1 (rows 8 j + lane / 8); B runs 2w, 2w + 1: run j is chunk
+  // j / 4 of rows 64 (j % 4) + lane; scale loads: waves 0-3 A rows 32 w +
+  // lane (lanes < 32), waves 4-7 B rows 64 (w - 4) + lane
+  uint32_t avo[2], bvo[2], svo;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int j = 2 * wave + u;
+    const int row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    avo[u] = (uint32_t)a_src(row) * (uint32_t)p.K + 16u * (uint32_t)c;
+    bvo[u] = (uint32_t)w_row(64 * (j & 3) + lane) * (uint32_t)(p.K / 2) + 16u * (uint32_t)(j >> 2);
+  }
+  if (wave < 4)
+    svo = (uint32_t)a_src(32 * wave + (lane & 31)) * ks;
+  else
+    svo = (uint32_t)w_row(64 * (wave - 4) + lane) * ks;
+  const bool s_up = MODE == kModeGateUp && wave >= 6;  // B scale rows 128..255: up
+
+  auto issue = [&](int it) {
+    const int buf = it % kStg;
+    const uint32_t ka = (uint32_t)it * kAB, kb = (uint32_t)it * kBB, kc = (uint32_t)it * 4u;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int j = 2 * wave + u;
+      lds_load16(ra, lds_offset(&s_a[buf][j * 1024]), avo[u] + ka);
+      lds_load16(MODE == kModeGateUp && (j & 3) >= 2 ? rb1 : rb0,
+                 lds_offset(&s_b[buf][(j >> 2) * (kWB * 16) + (j & 3) * 1024]), bvo[u] + kb);
+    }
+    if (wave < 4) {
+      if (lane < 32) lds_load4(ras, lds_offset(&s_as[buf][32 * wave]), svo + kc);
+    } else {
+      lds_load4(s_up ? rs1 : rs0, lds_offset(&s_bs[buf][64 * (wave - 4)]), svo + kc);
+    }
+  };
+
+  f32x4a_t acc[4][NB];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[m][nb] = (f32x4a_t){0.0f, 0.0f, 0.0f, 0.0f};
+
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  // live 16-row blocks of this wave's half
+  const int m_active = min(max((r1 - r0 - 64 * wh + 15) >> 4, 0), 4);
+  auto kloop = [&](auto ma_c) {
+    constexpr int MA = decltype(ma_c)::value;
+    for (int it = 0; it < nk; it++) {
+      if (it + 2 < nk) issue(it + 2);
+      if constexpr (MA > 0) {
+        const int buf = it % kStg;
+        const uint8_t *A = s_a[buf];
+        const uint8_t *B = s_b[buf];
+        i32x8_t bfr[NB];
+        int bsc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+          const int b = MODE == kModeGateUp ? (nb < 2 ? 0 : 128) + 32 * wc + 16 * (nb & 1) + lr
+                                            : 64 * wc + 16 * nb + lr;
+          const uint4 v = *reinterpret_cast<const uint4 *>(B + lg * (kWB * 16) + b * 16);
+          bfr[nb] = (i32x8_t){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          bsc[nb] = (int)((s_bs[buf][b] >> (8 * lg)) & 0xFFu);
+        }
+#pragma unroll
+        for (int m = 0; m < MA; m++) {
+          const int row = 64 * wh + 16 * m + lr;
+          const uint8_t *ar = A + row * kAB;
+          const int sw = (row >> 1) & 7;
+          const uint4 x0 = *reinterpret_cast<const uint4 *>(ar + 16 * (lg ^ sw));
+          const uint4 x1 = *reinterpret_cast<const uint4 *>(ar + 16 * ((4 + lg) ^ sw));
+          const i32x8_t af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                              (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          const int asc = (int)((s_as[buf][row] >> (8 * lg)) & 0xFFu);
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++)
+            acc[m][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af, bfr[nb], acc[m][nb], 0, 4, 0, asc, 0, bsc[nb]);
+        }
+      }
+      if (it + 1 < nk) {
+        if (it + 2 < nk)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma));
+        else
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+      }
+    }
+  };
+  if (m_active == 0)
+    kloop(std::integral_constant<int, 0>{});
+  else if (m_active <= 2)
+    kloop(std::integral_constant<int, 2>{});
+  else
+    kloop(std::integral_constant<int, 4>{});
+
+  // result register i of the lane: row 16 m + 4 (lane / 16) + i of the half,
+  // column lane % 16
+  constexpr int kWaveCols = MODE == kModeGateUp ? 32 : 64;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    if (m >= m_active) continue;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = r0 + 64 * wh + 16 * m + 4 * lg + i;
+      if constexpr (MODE == kModeGateUp) {
+        float a[2];
+        a[0] = silu_mul(acc[m][0][i], acc[m][2][i]);
+        a[1] = silu_mul(acc[m][1][i], acc[m][3][i]);
+        // the row's 32 columns of this wave are one MX-FP8 group: the 16
+        // lanes of this lane group hold them
+        float amax = fmaxf(fabsf(a[0]), fabsf(a[1]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const uint32_t e8 = mx8_scale_byte(amax);
+        const int sh = 127 - (int)e8;
+        if (r < r1) {
+          const size_t base = (size_t)r * p.N + n0 + kWaveCols * wc;
+#pragma unroll
+          for (int c = 0; c < 2; c++)
+            p.out_q[base + 16 * c + lr] =
+                (uint8_t)(amax > 0.0f ? e4m3_code(__builtin_ldexpf(a[c], sh)) : 0u);
+          if (p.a_f32) {
+#pragma unroll
+            for (int c = 0; c < 2; c++) p.a_f32[base + 16 * c + lr] = a[c];
+          }
+          if (lr == 0) p.out_s[(size_t)r * (p.N / 32) + (n0 + kWaveCols * wc) / 32] = (uint8_t)e8;
+        }
+      } else {
+        if (r < r1) {
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++)
+            p.y_out[(size_t)r * p.N + n0 + kWaveCols * wc + 16 * nb + lr] = acc[m][nb][i];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -374,8 +588,12 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   g.tiles = tiles, g.out_q = aq, g.out_s = as, g.a_f32 = a_trace;
   g.weight_major = !offsets && (I / a8_block_cols<kModeGateUp>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
-  err = launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
-               dim3(kA8Threads), s, g);
+  if constexpr (BM == 128)
+    err = launch(k_a8_dma<kModeGateUp>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
+                 dim3(kA8DmaThreads), s, g);
+  else
+    err = launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
+                 dim3(kA8Threads), s, g);
   if (err != hipSuccess) return err;
 
   A8Args d{};
@@ -383,8 +601,12 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   d.tiles = tiles, d.y_out = y;
   d.weight_major = !offsets && (H / a8_block_cols<kModeDown>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[2]);
-  return launch(k_gemm_a8<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
-                dim3(kA8Threads), s, d);
+  if constexpr (BM == 128)
+    return launch(k_a8_dma<kModeDown>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
+                  dim3(kA8DmaThreads), s, d);
+  else
+    return launch(k_gemm_a8<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
+                  dim3(kA8Threads), s, d);
 }
 
 }  // namespace
