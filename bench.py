@@ -80,13 +80,14 @@ KERNEL_OF = {"decode_p1": r"k_dec_p1<", "decode_p2": r"k_dec_p2<", "decode_p3": 
              "gemm_down": r"k_gemm(32)?<1, [123],", "combine": r"k_combine\b",
              "select": r"k_select\(", "select_plan": r"k_select_plan", "routed_gateup": r"k_gateup",
              "routed_down": r"k_down", "shared_gateup": r"k_gateup", "shared_down": r"k_down",
-             "a8_gemm_gateup": r"k_gemm_a8<0", "a8_gemm_down": r"k_gemm_a8<1",
+             "a8_gemm_gateup": r"k_(gemm_a8|a8_dma)<0", "a8_gemm_down": r"k_(gemm_a8|a8_dma)<1",
              "act_quant": r"k_mx8_quant", "tokens_f16": r"k_tokens_f16"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 # kernel symbol substring -> the source file it is built from
-SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm_a8", "gemm_fp4.hip"), ("k_mx8", "gemm_fp4.hip"),
+SOURCE_OF = (("k_dec_", "decode.hip"), ("k_gemm_a8", "gemm_fp4.hip"), ("k_a8_dma", "gemm_fp4.hip"),
+             ("k_mx8", "gemm_fp4.hip"), ("k_dense", "gemm.hip"),
              ("k_gemm", "gemm.hip"), ("k_tile_list", "gemm.hip"), ("k_tokens_f16", "gemm.hip"),
              ("k_skinny", "gemm.hip"), ("k_router", "route.hip"), ("k_select", "route.hip"),
              ("k_chunk", "route.hip"), ("k_plan", "route.hip"), ("k_gateup", "gemv.hip"),
