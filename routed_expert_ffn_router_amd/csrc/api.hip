@@ -261,6 +261,7 @@ struct FwdBufs {
   // large path
   int32_t *offsets, *sorted_slot;
   void *dispatch_ws;
+  float *wn2;
   FfnBufs ffn;
 };
 
@@ -307,6 +308,7 @@ FwdBufs carve_fwd(Carver &c, const moe_layer *L, int T, bool have_logits, bool h
     b.slot_pos = c.take<int32_t>(n);
     b.dispatch_ws = c.take<uint8_t>(dispatch_ws_bytes(T, E, k));
     b.y_rows = c.take<float>(n * H);
+    b.wn2 = c.take<float>(E);
     b.ffn = carve_ffn(c, T, (int)n, E, H, I, false, L->act_fmt);
   }
   return b;
@@ -601,7 +603,13 @@ static int forward_impl(const moe_layer *L, int T, const uint16_t *x, const floa
     const float *logits = logits_in;
     if (!logits) {
       mk("router");
-      MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
+      // the logits stay inside the call: many tokens take the screened router
+      if (!fwd_small(L, T) && router_screen_supported(H, E))
+        MOE_TRY(hip_check(launch_router_screened(L->route_mode, T, H, E, k, x, L->w_router,
+                                                 token_ids, b.logits, b.wn2, s),
+                          "router"));
+      else
+        MOE_TRY(hip_check(launch_router_logits(T, H, E, x, L->w_router, b.logits, s), "router"));
       logits = b.logits;
     }
     const WView g = view_of(L->gate), u = view_of(L->up), d = view_of(L->down);

@@ -82,6 +82,13 @@ inline size_t plan_ints(int max_active) { return 1 + 3 * (size_t)max_active; }
 // routing ------------------------------------------------------------------
 hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t *wr,
                                 float *logits, hipStream_t s);
+// Logits for the selection only: exact (as above) for the experts that can
+// reach the top k, -inf for the others; wn2: E floats of scratch.  Needs
+// router_screen_supported(H, E).
+bool router_screen_supported(int H, int E);
+hipError_t launch_router_screened(int mode, int T, int H, int E, int k, const uint16_t *x,
+                                  const uint16_t *wr, const int64_t *tids, float *logits,
+                                  float *wn2, hipStream_t s);
 // selection; when `plan` is non-null (T*k <= kSmallSlots) it also buckets
 // the slots: sorted_token/sorted_slot/slot_pos/row_w [T*k], offsets [E+1]
 // (optional) and the compact plan.

@@ -174,6 +174,295 @@ hipError_t launch_router_logits(int T, int H, int E, const uint16_t *x, const ui
 }
 
 // ----------------------------------------------------------------------------
+// screened router logits (many tokens; for the selection only)
+// ----------------------------------------------------------------------------
+// The selection needs exact logits only for the experts that can reach the
+// top k.  An fp32 approximation L~ from the bf16 matrix cores, with a rigorous
+// error bound delta, names the candidates
+//   C = { e : L~_e >= L~_(k) - 2 delta }     (L~_(k): the k-th largest L~)
+// and only their logits are computed exactly (fp64, as above); the others are
+// written as -inf.  An expert outside C has an exact, fp32-rounded logit
+// strictly below those of k experts in C, so it is outside the top k of the
+// full row whatever the tie rule, and the top k of the full row -- finite or
+// +inf, so above -inf -- are all in C: the selection and its softmax weights
+// are those of the full row, bit for bit.
+//
+// The bound.  A product of two bf16 is exact in fp32.  Any summation of H such
+// products with a unit roundoff u <= 2^-23 per step (rounded or truncated)
+// errs by at most gamma * sum |x_h w_h|, gamma = H u / (1 - H u) <= H 2^-22
+// while H u <= 1/2, and sum |x_h w_h| <= |x| |w_e| (Cauchy-Schwarz); flushed
+// subnormal products or partial sums add below 2 H 2^-126.  Rounding the exact
+// value L to fp32 moves it by at most 2^-24 |L| + 2^-150, and |L| <= max |L~| +
+// eps.  delta takes each of these twice.  |w_e|^2 comes from the approximation
+// kernel in fp32 (v_dot2, the same kind of bound), |x|^2 is summed in fp64.  A
+// row with a non-finite approximation, or one whose logits could leave the fp32
+// range, takes every expert as a candidate; in hash mode the candidates are the
+// k hashed experts and no approximation is made.
+
+typedef __bf16 bf16x8_rt __attribute__((ext_vector_type(8)));
+typedef float f32x16_rt __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_rt mfma_bf16_32(uint4 a, uint4 b, f32x16_rt c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_rt, a),
+                                                 __builtin_bit_cast(bf16x8_rt, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float sumsq8_bf16(uint4 v, float s) {
+  s = dot2_bf16(v.x, v.x, s);
+  s = dot2_bf16(v.y, v.y, s);
+  s = dot2_bf16(v.z, v.z, s);
+  return dot2_bf16(v.w, v.w, s);
+}
+
+// Approximate logits: block (bx, by) = tokens 32 by + [0, 32) x experts
+// 64 bx + [0, 64); its four waves take a quarter of H each and their partial
+// tiles are added in LDS in a fixed order.  v_mfma_f32_32x32x16_bf16 takes
+// A[l%32][8(l/32) + i] and B[8(l/32) + i][l%32] (i < 8) from lane l and leaves
+// D[8(q/4) + 4(l/32) + q%4][l%32] in its result register q.  The blocks of the
+// first token tile also write sum_h w[e][h]^2 for their experts into wn2.
+// E % 64 == 0, H % 64 == 0.
+__global__ __launch_bounds__(256) void k_router_approx(int T, int H, int E,
+                                                        const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wr,
+                                                        float *__restrict__ logits,
+                                                        float *__restrict__ wn2) {
+  __shared__ float red[4][32][64];
+  __shared__ float nrm[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, g = lane >> 5;
+  const int t0 = blockIdx.y * 32, e0 = blockIdx.x * 64;
+  const int hq = H / 4, h0 = wave * hq + 8 * g;
+  const int ta = min(t0 + r, T - 1);  // rows past T repeat the last token and are not stored
+  const uint4 *xa = reinterpret_cast<const uint4 *>(x + (size_t)ta * H + h0);
+  const uint4 *wb0 = reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + r) * H + h0);
+  const uint4 *wb1 = reinterpret_cast<const uint4 *>(wr + (size_t)(e0 + 32 + r) * H + h0);
+  const bool norms = blockIdx.y == 0;
+  const int n = hq / 16;
+  f32x16_rt c0 = {}, c1 = {};
+  float s0 = 0.0f, s1 = 0.0f;
+  constexpr int kP = 8;  // steps in flight
+  uint4 a[kP], b0[kP], b1[kP];
+#pragma unroll
+  for (int u = 0; u < kP; u++) {
+    const int i = min(u, n - 1);
+    a[u] = xa[2 * i], b0[u] = wb0[2 * i], b1[u] = wb1[2 * i];
+  }
+  for (int i0 = 0; i0 < n; i0 += kP) {
+#pragma unroll
+    for (int u = 0; u < kP; u++) {
+      if (i0 + u < n) {
+        c0 = mfma_bf16_32(a[u], b0[u], c0);
+        c1 = mfma_bf16_32(a[u], b1[u], c1);
+        if (norms) {
+          s0 = sumsq8_bf16(b0[u], s0);
+          s1 = sumsq8_bf16(b1[u], s1);
+        }
+      }
+      const int i = min(i0 + u + kP, n - 1);
+      a[u] = xa[2 * i], b0[u] = wb0[2 * i], b1[u] = wb1[2 * i];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    red[wave][q][lane] = c0[q];
+    red[wave][16 + q][lane] = c1[q];
+  }
+  if (norms) {
+    s0 += __shfl_xor(s0, 32, 64);
+    s1 += __shfl_xor(s1, 32, 64);
+    nrm[wave][lane] = lane < 32 ? s0 : s1;  // lane j: expert e0 + j
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const int reg = 8 * wave + q, i = reg & 15;
+    const float v = ((red[0][reg][lane] + red[1][reg][lane]) + red[2][reg][lane]) + red[3][reg][lane];
+    const int t = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
+    if (t < T) logits[(size_t)t * E + e0 + 32 * (reg >> 4) + r] = v;
+  }
+  if (norms && wave == 0)
+    wn2[e0 + lane] = ((nrm[0][lane] + nrm[1][lane]) + nrm[2][lane]) + nrm[3][lane];
+}
+
+__device__ __forceinline__ double dot8_bf16_f64_acc(uint4 a, uint4 b, double s) {
+  s = fma((double)bf16_lo(a.x), (double)bf16_lo(b.x), s);
+  s = fma((double)bf16_hi(a.x), (double)bf16_hi(b.x), s);
+  s = fma((double)bf16_lo(a.y), (double)bf16_lo(b.y), s);
+  s = fma((double)bf16_hi(a.y), (double)bf16_hi(b.y), s);
+  s = fma((double)bf16_lo(a.z), (double)bf16_lo(b.z), s);
+  s = fma((double)bf16_hi(a.z), (double)bf16_hi(b.z), s);
+  s = fma((double)bf16_lo(a.w), (double)bf16_lo(b.w), s);
+  return fma((double)bf16_hi(a.w), (double)bf16_hi(b.w), s);
+}
+
+// One wave per token: the candidates, their exact logits, -inf elsewhere,
+// written over the approximate row.  H = 512 NJ (lane l holds h = 8 l +
+// 512 j + [0, 8) of x), E % 64 == 0 and E <= 256 (expert lane + 64 i in slot i).
+template <int NJ>
+__global__ __launch_bounds__(256) void k_router_screen(int mode, int T, int E, int k,
+                                                        const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wr,
+                                                        const float *__restrict__ wn2,
+                                                        const int64_t *__restrict__ tids,
+                                                        float *__restrict__ logits) {
+  constexpr int H = 512 * NJ;
+  constexpr int G = NJ <= 8 ? 4 : 2;  // candidates per pass
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nc = E >> 6;
+  float *row = logits + (size_t)t * E;
+  uint4 xr[NJ];
+  const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * H) + lane;
+#pragma unroll
+  for (int j = 0; j < NJ; j++) xr[j] = xp[64 * j];
+  uint32_t cm = 0;  // bit i: expert lane + 64 i is a candidate
+  if (mode == MOE_ROUTE_HASH) {
+    const uint64_t z = splitmix64((uint64_t)tids[t]);
+    for (int j = 0; j < k; j++) {
+      const int e = (int)((z + (uint64_t)j) % (uint64_t)E);
+      if ((e & 63) == lane) cm |= 1u << (e >> 6);
+    }
+  } else {
+    float v[4];
+    bool bad = false;
+    float amax = 0.0f, wmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[i] = i < nc ? row[lane + 64 * i] : -INFINITY;
+      if (i < nc) {
+        bad |= !__builtin_isfinite(v[i]);
+        amax = fmaxf(amax, fabsf(v[i]));
+        wmax = fmaxf(wmax, wn2[lane + 64 * i]);
+      }
+    }
+    double sx = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) sx = dot8_bf16_f64_acc(xr[j], xr[j], sx);
+    sx = group_sum_f64<64>(sx);
+    const float M = wave_max_f(amax), W = wave_max_f(wmax);
+    const double gam = (double)H * 0x1p-22;
+    const double wb = ((double)W + (double)H * 0x1p-125) * (1.0 + 2.0 * gam);
+    const double S = sqrt(sx * wb) * (1.0 + 0x1p-40);
+    const double eps = gam * S + (double)H * 0x1p-125;
+    const double delta = eps + 0x1p-23 * ((double)M + eps) + 0x1p-149;
+    // also false for a NaN or infinite delta
+    const bool screen = __ballot(bad) == 0 && (double)M + 2.0 * delta < 0x1p127;
+    if (!screen) {
+      cm = (1u << nc) - 1u;
+    } else {
+      // the k-th largest approximate logit: each lane sorts its (at most four)
+      // values as order-preserving integer keys, then k rounds pop the
+      // largest head
+      int key[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) key[i] = float_key(v[i] + 0.0f);
+      auto order = [&](int p, int q) {
+        const int hi = max(key[p], key[q]), lo = min(key[p], key[q]);
+        key[p] = hi, key[q] = lo;
+      };
+      order(0, 1);
+      order(2, 3);
+      order(0, 2);
+      order(1, 3);
+      order(1, 2);
+      int kth = 0;
+      for (int j = 0; j < k; j++) {
+        kth = wave_max_all(key[0]);
+        const uint64_t at = __ballot(key[0] == kth);
+        if (lane == __builtin_ctzll(at)) {
+          key[0] = key[1], key[1] = key[2], key[2] = key[3];
+          key[3] = float_key(-INFINITY);
+        }
+      }
+      const double tau = (double)key_float(kth) - 2.0 * delta;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (i < nc && (double)v[i] >= tau) cm |= 1u << i;
+    }
+  }
+  // the candidates in expert order, G per pass, from the slot ballots
+  uint64_t m0 = __ballot(cm & 1u), m1 = __ballot(cm & 2u), m2 = __ballot(cm & 4u),
+           m3 = __ballot(cm & 8u);
+  auto next = [&]() -> int {
+    if (m0) { const int b = __builtin_ctzll(m0); m0 &= m0 - 1; return b; }
+    if (m1) { const int b = __builtin_ctzll(m1); m1 &= m1 - 1; return 64 + b; }
+    if (m2) { const int b = __builtin_ctzll(m2); m2 &= m2 - 1; return 128 + b; }
+    if (m3) { const int b = __builtin_ctzll(m3); m3 &= m3 - 1; return 192 + b; }
+    return -1;
+  };
+  float ex[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  int e_next = next();
+  while (e_next >= 0) {
+    int ids[G];
+    ids[0] = e_next;
+#pragma unroll
+    for (int u = 1; u < G; u++) {
+      const int e = next();
+      ids[u] = e >= 0 ? e : ids[u - 1];  // a repeat past the end: same value again
+    }
+    e_next = next();
+    double acc[G];
+#pragma unroll
+    for (int u = 0; u < G; u++) acc[u] = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; j++)
+#pragma unroll
+      for (int u = 0; u < G; u++) {
+        const uint4 wv = reinterpret_cast<const uint4 *>(wr + (size_t)ids[u] * H)[lane + 64 * j];
+        acc[u] = dot8_bf16_f64_acc(xr[j], wv, acc[u]);
+      }
+#pragma unroll
+    for (int u = 0; u < G; u++) {
+      const double s = group_sum_f64<64>(acc[u]);
+      if ((ids[u] & 63) == lane) {
+        const int sl = ids[u] >> 6;
+        const float f = (float)s;
+        ex[0] = sl == 0 ? f : ex[0];
+        ex[1] = sl == 1 ? f : ex[1];
+        ex[2] = sl == 2 ? f : ex[2];
+        ex[3] = sl == 3 ? f : ex[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (i < nc) row[lane + 64 * i] = ex[i];
+}
+
+bool router_screen_supported(int H, int E) {
+  return E % 64 == 0 && E <= 256 && H % 512 == 0 && H >= 512 && H <= 8192;
+}
+
+template <int NJ>
+static hipError_t launch_screen_nj(int mode, int T, int E, int k, const uint16_t *x,
+                                   const uint16_t *wr, const float *wn2, const int64_t *tids,
+                                   float *logits, hipStream_t s) {
+  return launch(k_router_screen<NJ>, dim3((T + 3) / 4), dim3(256), s, mode, T, E, k, x, wr, wn2,
+                tids, logits);
+}
+
+hipError_t launch_router_screened(int mode, int T, int H, int E, int k, const uint16_t *x,
+                                  const uint16_t *wr, const int64_t *tids, float *logits,
+                                  float *wn2, hipStream_t s) {
+  if (!router_screen_supported(H, E)) return hipErrorInvalidValue;
+  if (mode != MOE_ROUTE_HASH) {
+    const hipError_t e = launch(k_router_approx, dim3(E / 64, (T + 31) / 32), dim3(256), s, T, H,
+                                E, x, wr, logits, wn2);
+    if (e != hipSuccess) return e;
+  }
+  switch (H / 512) {
+#define MOE_SCREEN_CASE(n) \
+  case n: return launch_screen_nj<n>(mode, T, E, k, x, wr, wn2, tids, logits, s);
+    MOE_SCREEN_CASE(1) MOE_SCREEN_CASE(2) MOE_SCREEN_CASE(3) MOE_SCREEN_CASE(4)
+    MOE_SCREEN_CASE(5) MOE_SCREEN_CASE(6) MOE_SCREEN_CASE(7) MOE_SCREEN_CASE(8)
+    MOE_SCREEN_CASE(9) MOE_SCREEN_CASE(10) MOE_SCREEN_CASE(11) MOE_SCREEN_CASE(12)
+    MOE_SCREEN_CASE(13) MOE_SCREEN_CASE(14) MOE_SCREEN_CASE(15) MOE_SCREEN_CASE(16)
+#undef MOE_SCREEN_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
 // selection
 // ----------------------------------------------------------------------------
 

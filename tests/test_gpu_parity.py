@@ -983,6 +983,70 @@ def test_router_exactness_domain(dev):
 
 
 # --------------------------------------------------------------------------
+# the screened router of many-token forwards: exact and near ties among the
+# experts near the top, and tokens whose approximate logits are useless
+# (non-finite, zero, subnormal, near the end of the fp32 range)
+# --------------------------------------------------------------------------
+
+def _tie_router(wr):
+    """Rows 1 = row 0; rows 10..19 one row times 2 (a ten-way exact tie, most
+    often in the top 8); rows 30..37 one row times 1.5, each with one element
+    moved by one bf16 ulp (ties broken only in the last bits)."""
+    wr = wr.copy()
+    f = (wr.astype(np.uint32) << 16).view(np.float32)
+    wr[1] = wr[0]
+    wr[10:20] = synth.f32_to_bf16_bits(f[10] * 2)
+    near = synth.f32_to_bf16_bits(f[30] * 1.5)
+    for j in range(8):
+        row = near.copy()
+        row[7 * j + 3] += 1
+        wr[30 + j] = row
+    return wr
+
+
+def _odd_tokens(x, wr):
+    """Token rows 5..12 replaced by inputs outside the screen's comfort zone;
+    row 9 is router row 50 times 2.5 * 2^127, whose logit overflows fp32."""
+    f = (x.astype(np.uint32) << 16).view(np.float32).copy()
+    f[5, 17] = np.inf
+    f[6] *= np.float32(2.0 ** -120)
+    f[7] = 0
+    f[8] *= np.float32(2.0 ** 100)
+    f[9] = ((wr[50].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            * (2.5 * 2.0 ** 127)).astype(np.float32)
+    f[11] = f[10]
+    f[12, 3] = np.nan
+    return synth.f32_to_bf16_bits(f)
+
+
+@pytest.mark.parametrize("route", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
+def test_forward_screened_router_edges(dev, q2, dq2, route):
+    import dataclasses
+    T = 2048
+    wr = _tie_router(q2.w_router)
+    layer = dataclasses.replace(q2, w_router=wr)
+    dl = moe.DeviceLayer(dq2.H, dq2.I, dq2.E, dq2.k, route, t16(wr, dev), dq2.gate, dq2.up,
+                         dq2.down, dq2.shared_gate, dq2.shared_up, dq2.shared_down)
+    x = _odd_tokens(synth.gen_x(4096, T, seed=123), wr)
+    tids = synth.gen_token_ids(T, seed=124) if route == moe.ROUTE_HASH else None
+    out, idx, w = moe.forward(dl, t16(x, dev), None,
+                              None if tids is None else torch.from_numpy(tids).to(dev))
+    out, idx, w = tnp(out), tnp(idx), tnp(w)
+    R = oracle.LayerRef(layer, route_mode=route)
+    ridx, rw, rlo = R.route(x, None, tids)
+    assert np.array_equal(idx, ridx)
+    np.testing.assert_allclose(w, rw, rtol=1e-6, atol=1e-7, equal_nan=True)
+    if route == moe.ROUTE_SOFTMAX_TOPK:
+        # the ties did reach the top 8: exact ties decided by the index
+        tie = np.isin(ridx, np.arange(10, 20)).sum(1)
+        assert (tie == 8).sum() > 50 and list(ridx[7]) == list(range(8))
+        assert (np.isin(ridx, np.arange(30, 38)).sum(1) >= 2).sum() > 50
+    sel = np.array([0, 1, 2, 3, 4, 13, 1000, T - 1])
+    ref, _, _ = R.forward(x[sel], None, None if tids is None else tids[sel])
+    assert normwise(out[sel], ref) < TOL
+
+
+# --------------------------------------------------------------------------
 # speculative-decode verification batches: 1 + 5 tokens per session, one
 # session (T = 6) or 16 (T = 96), router or Zipf logits
 # --------------------------------------------------------------------------
