@@ -301,19 +301,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
   __shared__ uint32_t s_a[2][BM * kLdsRowW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
-  // XCD-aware order: workgroups go round-robin to the 8 XCDs (linear id b on
-  // XCD b % 8).  Grouped experts (a tile or two each): XCD x takes tiles x,
-  // x + 8, ... and walks all column blocks of a tile back to back, so its L2
-  // fetches each tile's rows once.  One dense expert over many tiles: XCD x
-  // takes column blocks x, x + 8, ... and walks all tiles of one back to back,
-  // so its L2 keeps that block of weights.  (grid.y, and grid.x in the dense
-  // order, are multiples of 8.)
-  const uint32_t nbx = gridDim.x, nby = gridDim.y;
-  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
-  const uint32_t jx = bid >> 3;
-  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
-  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
-  if (ti >= p.tiles[0]) return;
+  // XCD-aware block order (block_tile)
+  int ti, bx;
+  if (!block_tile(p.weight_major, p.tiles[0], &ti, &bx)) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
   const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
@@ -689,13 +679,9 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
   constexpr int kCbCopies = 32;
   __shared__ uint32_t s_a[kNBuf][BM * kAW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kCbCopies : 1];
-  // XCD-aware order, as in k_gemm
-  const uint32_t nbx = gridDim.x, nby = gridDim.y;
-  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
-  const uint32_t jx = bid >> 3;
-  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
-  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
-  if (ti >= p.tiles[0]) return;
+  // XCD-aware block order (block_tile)
+  int ti, bx;
+  if (!block_tile(p.weight_major, p.tiles[0], &ti, &bx)) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
   const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);

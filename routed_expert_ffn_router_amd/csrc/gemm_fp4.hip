@@ -135,13 +135,9 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * kA8Row];
   __shared__ uint32_t s_as[2][BM];  // the 4 scale bytes of each row and stage
 
-  // block -> (tile, column block), XCD-aware as in gemm.hip
-  const uint32_t nbx = gridDim.x, nby = gridDim.y;
-  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
-  const uint32_t jx = bid >> 3;
-  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
-  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
-  if (ti >= p.tiles[0]) return;
+  // XCD-aware block order (block_tile)
+  int ti, bx;
+  if (!block_tile(p.weight_major, p.tiles[0], &ti, &bx)) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
   const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
@@ -366,12 +362,8 @@ __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
   __shared__ __attribute__((aligned(16))) uint32_t s_as[kStg][BM];
   __shared__ __attribute__((aligned(16))) uint32_t s_bs[kStg][kWB];
 
-  const uint32_t nbx = gridDim.x, nby = gridDim.y;
-  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
-  const uint32_t jx = bid >> 3;
-  const int ti = p.weight_major ? (int)(jx % nby) : (int)((jx / nbx) * 8 + (bid & 7));
-  const int bx = p.weight_major ? (int)((jx / nby) * 8 + (bid & 7)) : (int)(jx % nbx);
-  if (ti >= p.tiles[0]) return;
+  int ti, bx;
+  if (!block_tile(p.weight_major, p.tiles[0], &ti, &bx)) return;
   const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
   const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
   const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);

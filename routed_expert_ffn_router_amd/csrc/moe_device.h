@@ -79,6 +79,35 @@ __device__ __forceinline__ double group_sum_f64(double v) {
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // --------------------------------------------------------------------------
+// block -> (row tile, column block) of the grouped GEMMs, XCD-aware:
+// workgroups go round-robin to the 8 XCDs (linear id b on XCD b % 8), each
+// with its own L2.
+//  * Grouped experts (rows first): XCD x takes the x-th eighth of the tile
+//    list in order and walks all column blocks of a tile back to back.  An
+//    expert's tiles are adjacent in the list, so they run together on one
+//    XCD and its weights are fetched into one L2 once, not once per tile.
+//  * One dense expert over many tiles (weight_major): XCD x takes column
+//    blocks x, x + 8, ... (grid.x a multiple of 8) and walks all tiles of
+//    one back to back, so its L2 keeps that block of weights.
+// grid.y is a multiple of 8 and at least n_tiles.  False for a block past the
+// real tiles.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ bool block_tile(bool weight_major, int n_tiles, int *ti, int *bx) {
+  const uint32_t nbx = gridDim.x, nby = gridDim.y;
+  const uint32_t bid = blockIdx.y * nbx + blockIdx.x;
+  const uint32_t jx = bid >> 3, x = bid & 7;
+  if (weight_major) {
+    *ti = (int)(jx % nby);
+    *bx = (int)((jx / nby) * 8 + x);
+    return *ti < n_tiles;
+  }
+  const int q = (int)(jx / nbx), per = (n_tiles + 7) >> 3;
+  *ti = (int)x * per + q;
+  *bx = (int)(jx % nbx);
+  return q < per && *ti < n_tiles;
+}
+
+// --------------------------------------------------------------------------
 // Q2K super-block (84 bytes): sc[16] | qs[64] | fp16 d | fp16 dmin
 // --------------------------------------------------------------------------
 constexpr int kQ2KBytes = 84;
