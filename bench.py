@@ -76,8 +76,8 @@ def _args():
 # GEMM markers take the routed weight formats only (Q2K, VQ2, MXFP4: template
 # argument 1, 2 or 3), not the shared expert's bf16 instance
 KERNEL_OF = {"decode_p1": r"k_dec_p1<", "decode_p2": r"k_dec_p2<", "decode_p3": r"k_dec_p3<",
-             "router": r"k_router", "gemm_gateup": r"k_gemm(32)?<0, [123],",
-             "gemm_down": r"k_gemm(32)?<1, [123],", "combine": r"k_combine\b",
+             "router": r"k_router", "gemm_gateup": r"k_gemm(32|_dma)?<0, [123],",
+             "gemm_down": r"k_gemm(32|_dma)?<1, [123],", "combine": r"k_combine\b",
              "select": r"k_select\(", "select_plan": r"k_select_plan", "routed_gateup": r"k_gateup",
              "routed_down": r"k_down", "shared_gateup": r"k_gateup", "shared_down": r"k_down",
              "a8_gemm_gateup": r"k_(gemm_a8|a8_dma)<0", "a8_gemm_down": r"k_(gemm_a8|a8_dma)<1",

@@ -906,6 +906,265 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 }
 
 // ---------------------------------------------------------------------------
+// The grouped GEMM with the token tile moved into LDS by direct loads
+// (buffer_load_dwordx4 ... lds), for the decoded formats.  One block of 8
+// waves per CU (two per SIMD): the waves share the codebook (32 copies, no
+// bank conflicts) and the A tile, and with no register holding a staged A
+// tile a block takes up to 96 rows (three 32-row MFMA blocks), so that an
+// expert bucket of 65..96 rows is one tile and its weights are decoded once.
+// Wave w covers output columns 32 w + [0, 32) of gate and up (gate/up, 256
+// a columns per block) or outputs 64 w + [0, 64) (down, 512 per block); the
+// B side (a lane's weight run, decoded into operand registers) is the one of
+// k_gemm32.
+//
+// A ring of 2 kSync stages in LDS.  Stage `it` holds, for every tile row, the
+// 64 k of k_gemm32's stage order (k = 256 G + 32 S + 128 (c / 32) + c % 32
+// for column c) in an unpadded 128-byte row whose 16-byte chunks are swizzled
+// by (row / 2) % 8.  A wave's load instruction fills 1 KB = 8 rows (lane i
+// writes slot i, so it fetches the global chunk that belongs at that slot);
+// wave w fills rows 8 w + [0, 8), and for 96-row tiles waves 0..3 also rows
+// 64 + 8 w + [0, 8).  Rows past the bucket read past the end of the buffer
+// and land as zeros.  Every kSync stages: wait for all of this wave's loads
+// (the kSync stages about to be read were issued kSync stages earlier, and
+// nothing newer is in flight), one barrier (every wave's loads are visible,
+// and every wave has left the previous kSync stages), then the loads of the
+// next kSync stages into the buffers those read.  With a barrier every
+// stage, the two waves of a SIMD (one block) waited on each other far more
+// often: the spacing is the measured best per format (dma_sync).  Past the
+// last stage the last one is loaded again (harmless, and simpler).
+// ---------------------------------------------------------------------------
+constexpr int kDmaThreads = 512;
+
+// stages per barrier (measured, same-box pairs): VQ2 / Q2K 96-row tiles two
+// (prefill 2048: gate/up 790 -> 715-740 us, down 542 -> 482-492 us against
+// k_gemm32's 64-row tiles; one barrier per stage: no gain, one per four:
+// gate/up 805-830 us); MXFP4 64-row tiles four (prefill 4096: 2775 -> 2660 us
+// per step; two per barrier: 2930 us)
+#ifndef MOE_DMA_SYNC
+#define MOE_DMA_SYNC 0
+#endif
+template <int FMT, int BM>
+constexpr int dma_sync() {
+  if (MOE_DMA_SYNC) return MOE_DMA_SYNC;
+  return FMT == MOE_FMT_MXFP4 ? 4 : 2;
+}
+
+template <int MODE>
+constexpr int dma_block_cols() { return MODE == kModeGateUp ? 256 : 512; }
+
+template <int FMT, int BM>
+struct DmaCfg {
+  static constexpr int kCb = FMT == MOE_FMT_VQ2 ? 32 : 0;  // codebook copies
+  static constexpr int kStage = BM * 128;                   // bytes per A stage
+  // four stages: stage 4 G + S sits in buffer S, an address the compiler
+  // knows (a ring of another length costs an address add per operand read)
+  static constexpr int kSync = dma_sync<FMT, BM>();
+  static constexpr int kNA = 2 * kSync;
+  static constexpr int kRuns = BM / 8;  // 1 KB runs per stage
+  static_assert(8 * 256 * kCb + kNA * kStage <= 163840, "LDS");
+};
+
+template <int MODE, int FMT, int OP, int BM>
+__global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmArgs p) {
+  static_assert(BM == 64 || BM == 96, "two or three 32-row blocks");
+  using Cfg = DmaCfg<FMT, BM>;
+  constexpr int MB = BM / 32;
+  constexpr int NB = 2;
+  constexpr int kNA = Cfg::kNA, kCb = Cfg::kCb, kRuns = Cfg::kRuns, kSync = Cfg::kSync;
+  __shared__ __attribute__((aligned(16))) uint32_t s_a[kNA][BM * 32];
+  __shared__ uint2 s_cb[kCb ? 256 * kCb : 1];
+  int ti, bx;
+  if (!block_tile(p.weight_major, p.tiles[0], &ti, &bx)) return;
+  const int e = __builtin_amdgcn_readfirstlane(p.tiles[1 + 3 * ti]);
+  const int r0 = __builtin_amdgcn_readfirstlane(p.tiles[2 + 3 * ti]);
+  const int r1 = __builtin_amdgcn_readfirstlane(p.tiles[3 + 3 * ti]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n0 = bx * dma_block_cols<MODE>();
+
+  if constexpr (FMT == MOE_FMT_VQ2) {  // codebook as exact fp16 integers, 32 copies
+    const int ent = tid & 255, half = tid >> 8;
+    const uint32_t cw = reinterpret_cast<const uint32_t *>(p.w0.codebook)[ent];
+    uint32_t hv[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+      hv[j] = pack_h2((float)(int)(int8_t)((cw >> (16 * j)) & 255u),
+                      (float)(int)(int8_t)((cw >> (16 * j + 8)) & 255u));
+#pragma unroll
+    for (int j = 0; j < kCb / 2; j++) {
+      const int c = kCb / 2 * half + j;
+      s_cb[ent * kCb + ((c + ent) & (kCb - 1))] = make_uint2(hv[0], hv[1]);
+    }
+  }
+
+  // this wave's A runs: run w, and run 8 + w where the tile has it
+  constexpr int kCh = (kRuns + 7) / 8;
+  const int n_ch = wave + 8 < kRuns ? 2 : 1;
+  const uint32_t a_bytes = (uint32_t)p.a_rows * (uint32_t)p.K * 2u;
+  const i32x4r_t ra = rsrc_words(MODE == kModeGateUp ? p.x : p.a16, a_bytes);
+  uint32_t a_vo[kCh];  // row offset + this lane's chunk offset within a stage
+#pragma unroll
+  for (int j = 0; j < kCh; j++) {
+    const int r = 8 * (8 * j + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);  // the global chunk for this slot
+    uint32_t vo = a_bytes;                       // past the end: zeros
+    if (r < BM && r0 + r < r1) {
+      const int src = (MODE == kModeGateUp && p.row_token) ? p.row_token[r0 + r] : r0 + r;
+      vo = (uint32_t)src * (uint32_t)p.K * 2u + 2u * (uint32_t)(128 * (c >> 2) + 8 * (c & 3));
+    }
+    a_vo[j] = vo;
+  }
+  const int nk = p.K / kBKs;
+  const int ng = nk / 4;
+  auto a_issue = [&](int it) {
+    const int st = min(it, nk - 1);
+    const uint32_t kb2 = 2u * (uint32_t)(256 * (st >> 2) + 32 * (st & 3));
+    const uint32_t base = lds_offset(&s_a[it & (kNA - 1)][0]);
+#pragma unroll
+    for (int j = 0; j < kCh; j++) {
+      if (j < n_ch) {
+        // rows past the bucket keep an offset past the end
+        const uint32_t vo = a_vo[j] >= a_bytes ? a_bytes : a_vo[j] + kb2;
+        lds_load16(ra, base + 1024u * (uint32_t)(8 * j + wave), vo);
+      }
+    }
+  };
+
+  constexpr int kWaveCols = MODE == kModeGateUp ? 32 : 64;
+  int wrow[NB];
+  const WView *wv[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    if constexpr (MODE == kModeGateUp) {
+      wrow[nb] = n0 + kWaveCols * wave + l32;
+      wv[nb] = nb == 0 ? &p.w0 : &p.w1;
+    } else {
+      wrow[nb] = n0 + kWaveCols * wave + 32 * nb + l32;
+      wv[nb] = &p.w0;
+    }
+  }
+
+  BRun<FMT, OP> gb0[NB], gb1[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) gb0[nb].load(*wv[nb], e, wrow[nb], 128 * h);
+#pragma unroll
+  for (int u = 0; u < kSync; u++) a_issue(u);
+
+  const int m_active = (r1 - r0 + 31) >> 5;
+  f32x16v_t acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; m++)
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[m][nb][i] = 0.0f;
+  const uint2 *cb = s_cb;
+
+  // B: VQ2 and Q2K decode one stage ahead into the other buffer of bp; MXFP4
+  // converts just before use
+  constexpr bool kJit = FMT == MOE_FMT_MXFP4;
+  uint32_t bp[kJit ? 1 : 2][NB][16];
+
+  auto kloop = [&](auto ma_c) {
+    constexpr int MA = decltype(ma_c)::value;
+    auto group = [&](int G, BRun<FMT, OP>(&cur)[NB], BRun<FMT, OP>(&nxt)[NB], auto par_c) {
+      constexpr int kPar = decltype(par_c)::value;
+#pragma unroll
+      for (int S = 0; S < 4; S++) {
+        const int it = 4 * G + S;
+        if (S % kSync == 0) {
+          // stages it .. it + kSync - 1 were loaded kSync stages ago and
+          // nothing newer is in flight
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+          __syncthreads();
+          if (S == 0) {
+            const int gn = min(G + 1, ng - 1);
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) nxt[nb].load(*wv[nb], e, wrow[nb], 256 * gn + 128 * h);
+          }
+#pragma unroll
+          for (int u = 0; u < kSync; u++) a_issue(it + kSync + u);
+        }
+        const uint32_t *A = s_a[kNA == 8 ? 4 * kPar + S : S];  // stage it's buffer, it % kNA
+        const int kCur = kJit ? 0 : (S & 1);
+        if constexpr (kJit) {
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++) cur[nb].decode(S, bp[0][nb], cb);
+        } else {
+          if (it == 0) {  // the codebook is in LDS after the first barrier
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) cur[nb].decode(0, bp[0][nb], cb);
+          }
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++) {
+            if (S < 3)
+              cur[nb].decode(S + 1, bp[(S + 1) & 1][nb], cb);
+            else
+              nxt[nb].decode(0, bp[(S + 1) & 1][nb], cb);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          uint4 af[MA];
+#pragma unroll
+          for (int m = 0; m < MA; m++)
+            af[m] = *reinterpret_cast<const uint4 *>(
+                &A[(32 * m + l32) * 32 + 4 * ((4 * h + t) ^ ((l32 >> 1) & 7))]);
+#pragma unroll
+          for (int m = 0; m < MA; m++)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+              const uint32_t *b = bp[kCur][nb];
+              const uint4 bf = make_uint4(b[4 * t], b[4 * t + 1], b[4 * t + 2], b[4 * t + 3]);
+              acc[m][nb] = mfma32<OP>(af[m], bf, acc[m][nb]);
+            }
+        }
+      }
+    };
+    for (int G = 0; G < ng; G += 2) {
+      group(G, gb0, gb1, std::integral_constant<int, 0>{});
+      if (G + 1 < ng) group(G + 1, gb1, gb0, std::integral_constant<int, 1>{});
+    }
+  };
+  if constexpr (MB == 2) {
+    if (m_active >= 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  } else {
+    if (m_active >= 3)
+      kloop(std::integral_constant<int, 3>{});
+    else if (m_active == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  }
+  // no load into LDS may be left in flight when the block ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    if (m >= m_active) continue;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int r = r0 + 32 * m + 8 * (i / 4) + 4 * h + (i % 4);
+      if (r >= r1) continue;
+      if constexpr (MODE == kModeGateUp) {
+        const float a = silu_mul(acc[m][0][i], acc[m][1][i]);
+        const int col = n0 + kWaveCols * wave + l32;
+        p.a_out[(size_t)r * p.N + (p.a_swap ? swap12(col) : col)] =
+            __builtin_bit_cast(uint16_t, (_Float16)a);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+          p.y_out[(size_t)r * p.N + n0 + kWaveCols * wave + 32 * nb + l32] = acc[m][nb][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // One dense bf16 expert over all T rows (the shared expert from 96 tokens),
 // with both operands staged in LDS by direct loads.  A block computes 128
 // rows against 256 weight rows: gate/up takes 128 gate and the 128 up rows of
@@ -1223,8 +1482,41 @@ namespace {
 // grid.x: the layer's output columns over the block's; grid.y: tiles.  Tiles
 // of 64 and 128 rows run the 32 x 32 x 16 instructions, 16-row tiles the
 // 16 x 16 x 32 ones
+// the direct-load kernel's formats and shapes
+bool dma_ok(int H, int I, int fmt_gate, int fmt_down) {
+  auto dec = [](int f) { return f == MOE_FMT_VQ2 || f == MOE_FMT_Q2K || f == MOE_FMT_MXFP4; };
+  return dec(fmt_gate) && dec(fmt_down) && I % dma_block_cols<kModeGateUp>() == 0 &&
+         H % dma_block_cols<kModeDown>() == 0;
+}
+// 96-row tiles always take it; 64-row tiles only for MXFP4 (VQ2 and Q2K:
+// k_gemm32 is as fast or faster there, prefill 4096 2645 vs 2660-2690 us)
+template <int BM>
+bool use_dma(int fmt) {
+  return BM == 96 || (BM == 64 && fmt == MOE_FMT_MXFP4);
+}
+
 template <int MODE, int BM>
-hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s) {
+hipError_t gemm_dma_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s) {
+#define MOE_DMA_CASE(F, O)                                                                    \
+  if (fmt == F && op == O)                                                                    \
+    return launch(k_gemm_dma<MODE, F, O, BM>, dim3(a.N / dma_block_cols<MODE>(), tiles),       \
+                  dim3(kDmaThreads), s, a);
+  MOE_DMA_CASE(MOE_FMT_VQ2, kOpF16)
+  MOE_DMA_CASE(MOE_FMT_Q2K, kOpF16)
+  MOE_DMA_CASE(MOE_FMT_MXFP4, kOpBF16)
+  MOE_DMA_CASE(MOE_FMT_MXFP4, kOpF16)
+#undef MOE_DMA_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int MODE, int BM>
+hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s, bool dma) {
+  if constexpr (BM == 64 || BM == 96) {
+    if (dma && use_dma<BM>(fmt)) return gemm_dma_fmt<MODE, BM>(a, fmt, op, tiles, s);
+  }
+  if constexpr (BM == 96) {
+    return hipErrorInvalidValue;
+  } else {
 #define MOE_GEMM_CASE(F, O)                                                                  \
   if (fmt == F && op == O) {                                                                 \
     if constexpr (BM >= 64)                                                                  \
@@ -1242,6 +1534,7 @@ hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s
   MOE_GEMM_CASE(MOE_FMT_MXFP4, kOpF16)
 #undef MOE_GEMM_CASE
   return hipErrorInvalidValue;
+  }
 }
 
 int gateup_op(int fmt) {
@@ -1255,6 +1548,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
                    hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
                    const char *const names[4]) {
   const int E = offsets ? gate.E : 0;
+  const bool dma = (BM == 64 || BM == 96) && offsets && dma_ok(H, I, gate.fmt, down.fmt);
   // tiles: sum over the active experts of ceil(rows / BM) <= n_rows / BM + the
   // active count, which is at most min(E, n_rows) (blocks past the real count
   // exit at once, but each still takes a slot and a load)
@@ -1293,7 +1587,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
     err = launch(k_dense<kModeGateUp>, dim3(I / dense_cols<kModeGateUp>(), (T + kDnRows - 1) / kDnRows),
                  dim3(kGemmThreads), s, da);
   } else {
-    err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s);
+    err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s, dma);
   }
   if (err != hipSuccess) return err;
 
@@ -1308,7 +1602,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
     return launch(k_dense<kModeDown>, dim3(H / dense_cols<kModeDown>(), (n_rows + kDnRows - 1) / kDnRows),
                   dim3(kGemmThreads), s, dd);
   }
-  return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, max_tiles, s);
+  return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, max_tiles, s, dma);
 }
 
 }  // namespace
@@ -1352,14 +1646,19 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
   if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
   if (gateup_op(gate.fmt) == kOpF16 && !x16) return hipErrorInvalidValue;
   // rows per tile: 128 for one dense expert of 96 rows or more (one wave per
-  // SIMD, each weight read for more rows), 64 from 32 rows per active expert,
-  // else 16.  Grouped experts stay at 64 even with 128 rows each: two tiles
-  // at two waves per SIMD beat one at one (prefill 4096, 128 rows per
-  // expert: VQ2 gate/up 1848 -> 1488 us, MXFP4 2175 -> 1779 us)
+  // SIMD, each weight read for more rows); 96 for grouped experts of 49..96
+  // rows each on average (most buckets one tile, the weights decoded once:
+  // prefill 2048, 64 rows per expert, 1486 -> 1375 us per step); 64 from 32
+  // rows per active expert; else 16.  Grouped experts stay at 64 with 128
+  // rows each: two tiles at two waves per SIMD beat one at one (prefill
+  // 4096: VQ2 gate/up 1848 -> 1488 us, MXFP4 2175 -> 1779 us)
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
   if (!offsets && n_rows >= 96)
     return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16,
                         x16, y, s, mark, mark_ctx, names);
+  if (offsets && dma_ok(H, I, gate.fmt, down.fmt) && n_rows > 48 * active && n_rows <= 96 * active)
+    return gemm_bm<96>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16,
+                       y, s, mark, mark_ctx, names);
   if (n_rows >= 32 * active)
     return gemm_bm<64>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16,
                        y, s, mark, mark_ctx, names);

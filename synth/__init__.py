@@ -93,6 +93,7 @@ WORKLOADS = {
         Workload("prefill_4096", Q2, 4096),
         Workload("mxfp4_decode_b1", MX, 1),
         Workload("mxfp4_hash_decode_b1", MX, 1, route=ROUTE_HASH),
+        Workload("mxfp4_prefill_2048", MX, 2048),
         Workload("mxfp4_prefill_4096", MX, 4096),
         Workload("mxfp4_hash_prefill_4096", MX, 4096, route=ROUTE_HASH),
         Workload("mxfp4_a8_prefill_4096", MX, 4096, act=1),
