@@ -910,8 +910,8 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 // (buffer_load_dwordx4 ... lds), for the decoded formats.  One block of 8
 // waves per CU (two per SIMD): the waves share the codebook (32 copies, no
 // bank conflicts) and the A tile, and with no register holding a staged A
-// tile a block takes up to 96 rows (three 32-row MFMA blocks), so that an
-// expert bucket of 65..96 rows is one tile and its weights are decoded once.
+// tile a block takes up to 128 rows (four 32-row MFMA blocks), so that most
+// expert buckets are one tile and their weights are decoded once.
 // Wave w covers output columns 32 w + [0, 32) of gate and up (gate/up, 256
 // a columns per block) or outputs 64 w + [0, 64) (down, 512 per block); the
 // B side (a lane's weight run, decoded into operand registers) is the one of
@@ -922,8 +922,8 @@ __global__ __launch_bounds__(kGemmThreads, BM == 64 ? 2 : 1) void k_gemm32(GemmA
 // for column c) in an unpadded 128-byte row whose 16-byte chunks are swizzled
 // by (row / 2) % 8.  A wave's load instruction fills 1 KB = 8 rows (lane i
 // writes slot i, so it fetches the global chunk that belongs at that slot);
-// wave w fills rows 8 w + [0, 8), and for 96-row tiles waves 0..3 also rows
-// 64 + 8 w + [0, 8).  Rows past the bucket read past the end of the buffer
+// wave w fills rows 8 w + [0, 8), and rows 64 + 8 w + [0, 8) where the tile
+// has them (96 rows: waves 0..3; 128 rows: all).  Rows past the bucket read past the end of the buffer
 // and land as zeros.  Every kSync stages: wait for all of this wave's loads
 // (the kSync stages about to be read were issued kSync stages earlier, and
 // nothing newer is in flight), one barrier (every wave's loads are visible,
@@ -966,7 +966,7 @@ struct DmaCfg {
 
 template <int MODE, int FMT, int OP, int BM>
 __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmArgs p) {
-  static_assert(BM == 64 || BM == 96, "two or three 32-row blocks");
+  static_assert(BM == 64 || BM == 96 || BM == 128, "two to four 32-row blocks");
   using Cfg = DmaCfg<FMT, BM>;
   constexpr int MB = BM / 32;
   constexpr int NB = 2;
@@ -1132,8 +1132,17 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmArgs p) {
       kloop(std::integral_constant<int, 2>{});
     else
       kloop(std::integral_constant<int, 1>{});
-  } else {
+  } else if constexpr (MB == 3) {
     if (m_active >= 3)
+      kloop(std::integral_constant<int, 3>{});
+    else if (m_active == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  } else {
+    if (m_active >= 4)
+      kloop(std::integral_constant<int, 4>{});
+    else if (m_active == 3)
       kloop(std::integral_constant<int, 3>{});
     else if (m_active == 2)
       kloop(std::integral_constant<int, 2>{});
@@ -1488,11 +1497,12 @@ bool dma_ok(int H, int I, int fmt_gate, int fmt_down) {
   return dec(fmt_gate) && dec(fmt_down) && I % dma_block_cols<kModeGateUp>() == 0 &&
          H % dma_block_cols<kModeDown>() == 0;
 }
-// 96-row tiles always take it; 64-row tiles only for MXFP4 (VQ2 and Q2K:
-// k_gemm32 is as fast or faster there, prefill 4096 2645 vs 2660-2690 us)
+// 96- and 128-row tiles always take it; 64-row tiles only for MXFP4 (VQ2
+// and Q2K: k_gemm32 is as fast or faster there, prefill 4096 from 64-row
+// tiles 2645 vs 2660-2690 us)
 template <int BM>
 bool use_dma(int fmt) {
-  return BM == 96 || (BM == 64 && fmt == MOE_FMT_MXFP4);
+  return BM == 96 || BM == 128 || (BM == 64 && fmt == MOE_FMT_MXFP4);
 }
 
 template <int MODE, int BM>
@@ -1511,7 +1521,7 @@ hipError_t gemm_dma_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream
 
 template <int MODE, int BM>
 hipError_t gemm_fmt(const GemmArgs &a, int fmt, int op, int tiles, hipStream_t s, bool dma) {
-  if constexpr (BM == 64 || BM == 96) {
+  if constexpr (BM == 64 || BM == 96 || BM == 128) {
     if (dma && use_dma<BM>(fmt)) return gemm_dma_fmt<MODE, BM>(a, fmt, op, tiles, s);
   }
   if constexpr (BM == 96) {
@@ -1548,7 +1558,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
                    hipStream_t s, void (*mark)(void *, const char *), void *mark_ctx,
                    const char *const names[4]) {
   const int E = offsets ? gate.E : 0;
-  const bool dma = (BM == 64 || BM == 96) && offsets && dma_ok(H, I, gate.fmt, down.fmt);
+  const bool dma = (BM == 64 || BM == 96 || BM == 128) && offsets && dma_ok(H, I, gate.fmt, down.fmt);
   // tiles: sum over the active experts of ceil(rows / BM) <= n_rows / BM + the
   // active count, which is at most min(E, n_rows) (blocks past the real count
   // exit at once, but each still takes a slot and a load)
@@ -1645,18 +1655,21 @@ hipError_t launch_gemm_ffn(const WView &gate, const WView &up, const WView &down
                            const char *const names[4]) {
   if (!gemm_supported(H, I, gate.fmt, down.fmt) || n_rows < 1 || T < 1) return hipErrorInvalidValue;
   if (gateup_op(gate.fmt) == kOpF16 && !x16) return hipErrorInvalidValue;
-  // rows per tile: 128 for one dense expert of 96 rows or more (one wave per
-  // SIMD, each weight read for more rows); 96 for grouped experts of 49..96
-  // rows each on average (most buckets one tile, the weights decoded once:
-  // prefill 2048, 64 rows per expert, 1486 -> 1375 us per step); 64 from 32
-  // rows per active expert; else 16.  Grouped experts stay at 64 with 128
-  // rows each: two tiles at two waves per SIMD beat one at one (prefill
-  // 4096: VQ2 gate/up 1848 -> 1488 us, MXFP4 2175 -> 1779 us)
+  // rows per tile: 128 for one dense expert of 96 rows or more (k_dense);
+  // for grouped experts in a decoded format (k_gemm_dma, two waves per SIMD,
+  // the token tile in LDS only), 128 above 96 rows per active expert and 96
+  // from 49 (most buckets one tile, each expert's weights decoded about once
+  // instead of 1.5 or 2.5 times: prefill 2048, 64 rows per expert, 1486 ->
+  // 1375 us per step; prefill 4096, 128 rows, 2651 -> 2492 us); otherwise 64
+  // from 32 rows per active expert (k_gemm32), else 16
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
   if (!offsets && n_rows >= 96)
     return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16,
                         x16, y, s, mark, mark_ctx, names);
-  if (offsets && dma_ok(H, I, gate.fmt, down.fmt) && n_rows > 48 * active && n_rows <= 96 * active)
+  if (offsets && dma_ok(H, I, gate.fmt, down.fmt) && n_rows > 96 * active)
+    return gemm_bm<128>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16,
+                        y, s, mark, mark_ctx, names);
+  if (offsets && dma_ok(H, I, gate.fmt, down.fmt) && n_rows > 48 * active)
     return gemm_bm<96>(gate, up, down, H, I, T, x, offsets, sorted_token, n_rows, tiles, a16, x16,
                        y, s, mark, mark_ctx, names);
   if (n_rows >= 32 * active)

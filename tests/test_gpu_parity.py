@@ -515,6 +515,49 @@ def test_expert_ffn_gemm_ragged_buckets_128(dev, q2, dq2):
     assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 93) < TOL
 
 
+@pytest.mark.parametrize("fmt", ["q2", "mx"])
+def test_expert_ffn_gemm_ragged_buckets_64(dev, q2, dq2, mx, dmx, fmt):
+    """Bucket sizes around the 64-row tile, 33..48 rows per active expert on
+    average (VQ2 / Q2K: the register-staged tiles; MXFP4: the direct-load
+    ones)."""
+    layer, dl = (q2, dq2) if fmt == "q2" else (mx, dmx)
+    sizes = np.array([0, 1, 31, 32, 33, 40, 47, 48, 49, 63, 64, 65] * 22)[:256]
+    active = (sizes > 0).sum()
+    assert 32 * active <= sizes.sum() <= 48 * active
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 97
+    st = np.random.default_rng(9).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=98)
+    assert _gemm_rows_case(layer, dl, dev, x, off, st, 64, 99) < TOL
+
+
+def test_expert_ffn_gemm_ragged_buckets_96(dev, q2, dq2):
+    """Bucket sizes around the 96- and 128-row tiles, 49..96 rows per active
+    expert on average: one, two or three tiles per expert, each with one to
+    three live 32-row blocks."""
+    sizes = np.array([0, 1, 31, 32, 33, 64, 95, 96, 97, 128, 160, 193] * 22)[:256]
+    active = (sizes > 0).sum()
+    assert 48 * active < sizes.sum() <= 96 * active
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 97
+    st = np.random.default_rng(7).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=94)
+    assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 95) < TOL
+
+
+def test_expert_ffn_gemm_ragged_buckets_128_tiles(dev, q2, dq2):
+    """Bucket sizes around the 128-row tile, more than 96 rows per active
+    expert on average: one to three tiles per expert, one to four live
+    32-row blocks each."""
+    sizes = np.array([1, 32, 96, 97, 127, 128, 129, 160, 200, 255, 256, 257] * 22)[:256]
+    assert sizes.sum() > 96 * (sizes > 0).sum()
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 97
+    st = np.random.default_rng(8).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=96)
+    assert _gemm_rows_case(q2, dq2, dev, x, off, st, 64, 97) < TOL
+
+
 @pytest.mark.parametrize("T", [2, 16, 33, 64, 97, 1100])
 def test_expert_ffn_dense_shared_gemm(dev, q2, dq2, T):
     x = synth.gen_x(4096, T, seed=T)
