@@ -171,7 +171,12 @@ int moe_abi_version(void);
  * topk_idx: int32 [T][k] out; topk_w: fp32 [T][k] out (softmax weights in
  *   selection order); logits_out: optional fp32 [T][E] out.
  * ws: scratch of moe_route_workspace(T, E) bytes (may be 0 when logits_out
- *   or logits_in is given).  1 <= k <= min(E, 16); E <= 1024. */
+ *   or logits_in is given).  1 <= k <= min(E, 16); E <= 1024.
+ * Without logits_in and logits_out, above 1024 (token, choice) slots (E a
+ *   multiple of 64 up to 256, H a multiple of 512 up to 8192), the logits
+ *   are computed exactly only for the experts whose bf16 matrix-core
+ *   approximation, with a rigorous error bound, can reach the top k; the
+ *   selected experts and weights are the same bit for bit. */
 size_t moe_route_workspace(int T, int E);
 int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uint16_t *w_router,
               const float *logits_in, const int64_t *token_ids, int32_t *topk_idx, float *topk_w,

@@ -365,7 +365,9 @@ int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
 size_t moe_route_workspace(int T, int E) {
   if (T < 0 || E < 1) return 0;
-  return ((size_t)T * E * sizeof(float) + 255) & ~size_t(255);
+  // the logits, then the screened router's E floats
+  return (((size_t)T * E * sizeof(float) + 255) & ~size_t(255)) +
+         (((size_t)E * sizeof(float) + 255) & ~size_t(255));
 }
 
 int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uint16_t *w_router,
@@ -388,7 +390,17 @@ int moe_route(int mode, int T, int H, int E, int k, const uint16_t *x, const uin
                     moe_route_workspace(T, E));
       dst = static_cast<float *>(ws);
     }
-    MOE_TRY(hip_check(launch_router_logits(T, H, E, x, w_router, dst, s), "router"));
+    // logits that stay inside the call, for many tokens: the screened router
+    // (exact logits for the experts that can reach the top k, -inf for the
+    // others; the selection is the same)
+    if (!logits_out && (long long)T * k > kSmallSlots && router_screen_supported(H, E)) {
+      float *wn2 = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                             (((size_t)T * E * sizeof(float) + 255) & ~size_t(255)));
+      MOE_TRY(hip_check(launch_router_screened(mode, T, H, E, k, x, w_router, token_ids, dst, wn2, s),
+                        "router"));
+    } else {
+      MOE_TRY(hip_check(launch_router_logits(T, H, E, x, w_router, dst, s), "router"));
+    }
     lsrc = dst;
   } else if (logits_out) {
     MOE_TRY(hip_check(hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),

@@ -113,6 +113,26 @@ def test_router_softmax_topk(dev, q2, T):
     np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("mode", [moe.ROUTE_SOFTMAX_TOPK, moe.ROUTE_HASH])
+def test_router_screened_no_logits(dev, q2, mode):
+    """moe_route without a logits output at 2048 tokens takes the screened
+    router: the same indices and weights as the oracle's exact logits."""
+    T = 2048
+    x = synth.gen_x(4096, T, seed=111)
+    tids = synth.gen_token_ids(T, seed=112) if mode == moe.ROUTE_HASH else None
+    idx, w, lo = moe.route(t16(x, dev), t16(q2.w_router, dev), 8, mode=mode,
+                           token_ids=None if tids is None else torch.from_numpy(tids).to(dev),
+                           want_logits=False)
+    assert lo is None
+    ref_lo = oracle.router_logits(x, q2.w_router)
+    if mode == moe.ROUTE_HASH:
+        ref_idx, ref_w = oracle.select_hash(tids, ref_lo, 8)
+    else:
+        ref_idx, ref_w = oracle.select_topk(ref_lo, 8)
+    assert np.array_equal(tnp(idx), ref_idx)
+    np.testing.assert_allclose(tnp(w), ref_w, rtol=1e-6, atol=1e-7)
+
+
 def test_router_tiny(dev, tiny):
     x = synth.gen_x(256, 4, seed=0)
     idx, w, lo = moe.route(t16(x, dev), t16(tiny.w_router, dev), 2)
