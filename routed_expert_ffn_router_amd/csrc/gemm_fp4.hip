@@ -352,11 +352,17 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
 // ---------------------------------------------------------------------------
 constexpr int kA8DmaThreads = 512;
 
-template <int MODE>
+template <int MODE, int BM>
 __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
-  constexpr int BM = 128, NB = 4, kStg = 3, kWB = 256;
+  static_assert(BM == 128 || BM == 192, "tile rows");
+  constexpr int NB = 4, kStg = 3, kWB = 256;
+  constexpr int RH = BM / 2, MB = RH / 16;   // rows per wave half, 16-row blocks
+  constexpr int kAR = BM / 64;               // A runs (8 rows of 128 bytes) per wave
   constexpr int kAB = kA8K, kBB = kA8K / 2;  // A and B bytes per row and stage
-  constexpr int kDma = 5;                    // direct loads per wave and stage
+  // direct loads per wave and stage: A runs, 2 B runs, and the scales (128:
+  // one load, A rows on waves 0-3, B rows on 4-7; 192: an A and a B load on
+  // every wave)
+  constexpr int kDma = kAR + 2 + (BM == 128 ? 1 : 2);
   __shared__ __attribute__((aligned(16))) uint8_t s_a[kStg][BM * kAB];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[kStg][kWB * kBB];
   __shared__ __attribute__((aligned(16))) uint32_t s_as[kStg][BM];
@@ -392,44 +398,63 @@ __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
   // weight row of LDS B row b (gate/up: rows below 128 gate, the rest up)
   auto w_row = [&](int b) { return n0 + (MODE == kModeGateUp ? (b & 127) : b); };
 
-  // A runs 2w, 2w + 1 (rows 8 j + lane / 8); B runs 2w, 2w + 1: run j is chunk
-  // j / 4 of rows 64 (j % 4) + lane; scale loads: waves 0-3 A rows 32 w +
-  // lane (lanes < 32), waves 4-7 B rows 64 (w - 4) + lane
-  uint32_t avo[2], bvo[2], svo;
+  // A runs kAR w + u (rows 8 j + lane / 8); B runs 2w, 2w + 1: run j is chunk
+  // j / 4 of rows 64 (j % 4) + lane.  Scale loads, 128: waves 0-3 A rows
+  // 32 w + lane (lanes < 32), waves 4-7 B rows 64 (w - 4) + lane; 192: A rows
+  // 24 w + lane (lanes < 24) and B rows 32 w + lane (lanes < 32)
+  uint32_t avo[kAR], bvo[2], svo, svo_b = 0;
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int j = 2 * wave + u;
+  for (int u = 0; u < kAR; u++) {
+    const int j = kAR * wave + u;
     const int row = 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     avo[u] = (uint32_t)a_src(row) * (uint32_t)p.K + 16u * (uint32_t)c;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int j = 2 * wave + u;
     bvo[u] = (uint32_t)w_row(64 * (j & 3) + lane) * (uint32_t)(p.K / 2) + 16u * (uint32_t)(j >> 2);
   }
-  if (wave < 4)
-    svo = (uint32_t)a_src(32 * wave + (lane & 31)) * ks;
-  else
-    svo = (uint32_t)w_row(64 * (wave - 4) + lane) * ks;
-  const bool s_up = MODE == kModeGateUp && wave >= 6;  // B scale rows 128..255: up
+  bool s_up;  // this wave's B scale rows are up rows (128..255)
+  if constexpr (BM == 128) {
+    if (wave < 4)
+      svo = (uint32_t)a_src(32 * wave + (lane & 31)) * ks;
+    else
+      svo = (uint32_t)w_row(64 * (wave - 4) + lane) * ks;
+    s_up = MODE == kModeGateUp && wave >= 6;
+  } else {
+    svo = (uint32_t)a_src(24 * wave + min(lane, 23)) * ks;
+    svo_b = (uint32_t)w_row(32 * wave + (lane & 31)) * ks;
+    s_up = MODE == kModeGateUp && wave >= 4;
+  }
 
   auto issue = [&](int it) {
     const int buf = it % kStg;
     const uint32_t ka = (uint32_t)it * kAB, kb = (uint32_t)it * kBB, kc = (uint32_t)it * 4u;
 #pragma unroll
+    for (int u = 0; u < kAR; u++)
+      lds_load16(ra, lds_offset(&s_a[buf][(kAR * wave + u) * 1024]), avo[u] + ka);
+#pragma unroll
     for (int u = 0; u < 2; u++) {
       const int j = 2 * wave + u;
-      lds_load16(ra, lds_offset(&s_a[buf][j * 1024]), avo[u] + ka);
       lds_load16(MODE == kModeGateUp && (j & 3) >= 2 ? rb1 : rb0,
                  lds_offset(&s_b[buf][(j >> 2) * (kWB * 16) + (j & 3) * 1024]), bvo[u] + kb);
     }
-    if (wave < 4) {
-      if (lane < 32) lds_load4(ras, lds_offset(&s_as[buf][32 * wave]), svo + kc);
+    if constexpr (BM == 128) {
+      if (wave < 4) {
+        if (lane < 32) lds_load4(ras, lds_offset(&s_as[buf][32 * wave]), svo + kc);
+      } else {
+        lds_load4(s_up ? rs1 : rs0, lds_offset(&s_bs[buf][64 * (wave - 4)]), svo + kc);
+      }
     } else {
-      lds_load4(s_up ? rs1 : rs0, lds_offset(&s_bs[buf][64 * (wave - 4)]), svo + kc);
+      if (lane < 24) lds_load4(ras, lds_offset(&s_as[buf][24 * wave]), svo + kc);
+      if (lane < 32) lds_load4(s_up ? rs1 : rs0, lds_offset(&s_bs[buf][32 * wave]), svo_b + kc);
     }
   };
 
-  f32x4a_t acc[4][NB];
+  f32x4a_t acc[MB][NB];
 #pragma unroll
-  for (int m = 0; m < 4; m++)
+  for (int m = 0; m < MB; m++)
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) acc[m][nb] = (f32x4a_t){0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -442,7 +467,7 @@ __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
   __syncthreads();
 
   // live 16-row blocks of this wave's half
-  const int m_active = min(max((r1 - r0 - 64 * wh + 15) >> 4, 0), 4);
+  const int m_active = min(max((r1 - r0 - RH * wh + 15) >> 4, 0), MB);
   auto kloop = [&](auto ma_c) {
     constexpr int MA = decltype(ma_c)::value;
     for (int it = 0; it < nk; it++) {
@@ -463,7 +488,7 @@ __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
         }
 #pragma unroll
         for (int m = 0; m < MA; m++) {
-          const int row = 64 * wh + 16 * m + lr;
+          const int row = RH * wh + 16 * m + lr;
           const uint8_t *ar = A + row * kAB;
           const int sw = (row >> 1) & 7;
           const uint4 x0 = *reinterpret_cast<const uint4 *>(ar + 16 * (lg ^ sw));
@@ -490,18 +515,20 @@ __global__ __launch_bounds__(kA8DmaThreads, 1) void k_a8_dma(A8Args p) {
     kloop(std::integral_constant<int, 0>{});
   else if (m_active <= 2)
     kloop(std::integral_constant<int, 2>{});
-  else
+  else if (MB == 4 || m_active <= 4)
     kloop(std::integral_constant<int, 4>{});
+  else
+    kloop(std::integral_constant<int, MB>{});
 
   // result register i of the lane: row 16 m + 4 (lane / 16) + i of the half,
   // column lane % 16
   constexpr int kWaveCols = MODE == kModeGateUp ? 32 : 64;
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
+  for (int m = 0; m < MB; m++) {
     if (m >= m_active) continue;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int r = r0 + 64 * wh + 16 * m + 4 * lg + i;
+      const int r = r0 + RH * wh + 16 * m + 4 * lg + i;
       if constexpr (MODE == kModeGateUp) {
         float a[2];
         a[0] = silu_mul(acc[m][0][i], acc[m][2][i]);
@@ -580,8 +607,8 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   g.tiles = tiles, g.out_q = aq, g.out_s = as, g.a_f32 = a_trace;
   g.weight_major = !offsets && (I / a8_block_cols<kModeGateUp>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[1]);
-  if constexpr (BM == 128)
-    err = launch(k_a8_dma<kModeGateUp>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
+  if constexpr (BM >= 128)
+    err = launch(k_a8_dma<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
                  dim3(kA8DmaThreads), s, g);
   else
     err = launch(k_gemm_a8<kModeGateUp, BM>, dim3(I / a8_block_cols<kModeGateUp>(), max_tiles),
@@ -593,8 +620,8 @@ hipError_t a8_bm(const WView &gate, const WView &up, const WView &down, int H, i
   d.tiles = tiles, d.y_out = y;
   d.weight_major = !offsets && (H / a8_block_cols<kModeDown>()) % 8 == 0 && max_tiles >= 16;
   if (mark) mark(mark_ctx, names[2]);
-  if constexpr (BM == 128)
-    return launch(k_a8_dma<kModeDown>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
+  if constexpr (BM >= 128)
+    return launch(k_a8_dma<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
                   dim3(kA8DmaThreads), s, d);
   else
     return launch(k_gemm_a8<kModeDown, BM>, dim3(H / a8_block_cols<kModeDown>(), max_tiles),
@@ -626,8 +653,14 @@ hipError_t launch_a8_ffn(const WView &gate, const WView &up, const WView &down, 
       launch(k_mx8_quant, dim3((unsigned)((n8 + 255) / 256)), dim3(256), s, T, H, x, xq, xs);
   if (err != hipSuccess) return err;
   const int active = offsets ? (gate.E < n_rows ? gate.E : n_rows) : 1;
-  // 128-row tiles from 96 rows per active expert: each expert's weights then
-  // stream about once per bucket rather than once per 64 rows
+  // 192-row tiles from 112 rows per active expert: a bucket of up to 192 rows
+  // (prefill 4096: 128 +- 11) is one tile, so each expert's weights stream
+  // once instead of once more for the few rows past 128; 128-row tiles from
+  // 96 rows: the weights stream about once per bucket rather than once per 64
+  // rows
+  if (n_rows >= 112 * active)
+    return a8_bm<192>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq,
+                      as, a_trace, y, s, mark, mark_ctx, names);
   if (n_rows >= 96 * active)
     return a8_bm<128>(gate, up, down, H, I, T, offsets, sorted_token, n_rows, tiles, xq, xs, aq,
                       as, a_trace, y, s, mark, mark_ctx, names);

@@ -776,6 +776,52 @@ def test_mxfp8_quantize_bit_exact(dev):
     assert np.array_equal(tnp(q), rq)
 
 
+def _a8_rows_case(layer, dl, dev, x, off, st, rows):
+    """moe_expert_ffn with MX-FP8 activations over the buckets (off, st); the
+    bucket rows `rows`: their quantized SwiGLU output (_check_a8_codes) and
+    their y rows against the oracle's down projection of the GPU's codes."""
+    spec = layer.spec
+    T, n = x.shape[0], int(off[-1])
+    y, ws = moe.expert_ffn(t16(x, dev), dl.gate, dl.up, dl.down, torch.from_numpy(off).to(dev),
+                           torch.from_numpy(st).to(dev), act=moe.ACT_MXFP8 | moe.ACT_TRACE,
+                           keep_ws=True)
+    gc, gs, gv = moe.a8_intermediate(ws, T, n, spec.E, spec.H, spec.I)
+    gc, gs, gv, y = tnp(gc), tnp(gs), tnp(gv), tnp(y)
+    y2 = tnp(moe.expert_ffn(t16(x, dev), dl.gate, dl.up, dl.down, torch.from_numpy(off).to(dev),
+                            torch.from_numpy(st).to(dev), act=moe.ACT_MXFP8))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    assert np.isfinite(y).all()
+    rows, sub_off, sub_st = _sub_buckets(off, st, rows)
+    _check_a8_codes(layer, x, sub_off, sub_st, gc[rows], gs[rows], gv[rows])
+    y_ref = oracle.LayerRef(layer).a8_down(sub_off, gc[rows], gs[rows])
+    return normwise(y[rows], y_ref)
+
+
+@pytest.mark.parametrize("tile", [128, 192])
+def test_expert_ffn_a8_ragged_buckets(dev, mx, dmx, tile):
+    """MX-FP8 GEMMs on bucket sizes around their tiles: more than 112 rows per
+    active expert on average (192-row tiles: one or two per expert, a wave
+    half of 96 rows with zero to six live 16-row blocks), or 96..112 (128-row
+    tiles).  Checked rows: the first and last of each bucket and those at the
+    wave-half and tile boundaries (64, 96, 128, 192 rows in)."""
+    if tile == 192:
+        sizes = np.array([1, 97, 112, 128, 129, 150, 176, 191, 192, 193, 200, 0] * 22)[:256]
+        assert sizes.sum() >= 112 * 256  # the host's test: rows per min(E, rows)
+    else:
+        sizes = np.array([1, 64, 96, 97, 100, 120, 127, 128, 129, 140, 0, 160] * 22)[:256]
+        assert 96 * 256 <= sizes.sum() < 112 * 256
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = 211
+    st = np.random.default_rng(tile).integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.gen_x(4096, T, seed=tile + 1)
+    rows = []
+    for e in range(12):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows += [r for r in (r0, r0 + 63, r0 + 64, r0 + 95, r0 + 96, r0 + 127, r0 + 128,
+                             r0 + 191, r0 + 192, r1 - 1) if r0 <= r < r1]
+    assert _a8_rows_case(mx, dmx, dev, x, off, st, rows) < TOL
+
+
 @pytest.mark.parametrize("T", [1, 3, 40, 300])
 def test_forward_mxfp4_a8(dev, mx, dmx, T):
     _forward_case(mx, dmx.with_act(moe.ACT_MXFP8), dev, T, 500 + T, a8=True)
