@@ -1177,14 +1177,16 @@ __global__ __launch_bounds__(kDmaThreads, 1) void k_gemm_dma(GemmArgs p) {
 // One dense bf16 expert over all T rows (the shared expert from 96 tokens),
 // with both operands staged in LDS by direct loads.  A block computes 128
 // rows against 256 weight rows: gate/up takes 128 gate and the 128 up rows of
-// the same SwiGLU columns (wave w: columns 32 w + [0, 32) of both), down 256
-// outputs (wave w: outputs 64 w + [0, 64)); every wave covers all 128 rows
-// (4 x 2 accumulators of 32 x 32).  buffer_load_dwordx4 ... lds moves 16
-// bytes per lane from global memory into LDS (lane i of a wave's load writes
-// slot i of a 1 KB run, from whatever global address the lane names), three
-// K stages of 64 deep, so no register holds a staged tile and the matrix
-// instructions of one wave per SIMD have a whole stage of loads ahead of
-// them.  LDS rows are 128 bytes, unpadded, 16-byte chunks XOR-swizzled by
+// the same SwiGLU columns (column group c = w % 4: columns 32 c + [0, 32) of
+// both), down 256 outputs (group c: outputs 64 c + [0, 64)); wave w covers
+// rows 64 (w / 4) + [0, 64) of its group (2 x 2 accumulators of 32 x 32).
+// Eight waves, two per SIMD: with four (each all 128 rows, one per SIMD)
+// gate/up took 81-83 us at 2048 rows against 69-71 us.  buffer_load_dwordx4
+// ... lds moves 16 bytes per lane from global memory into LDS (lane i of a
+// wave's load writes slot i of a 1 KB run, from whatever global address the
+// lane names), three K stages of 64 deep, so no register holds a staged tile
+// and the matrix instructions have a whole stage of loads ahead of them.
+// LDS rows are 128 bytes, unpadded, 16-byte chunks XOR-swizzled by
 // (row / 2) % 8 (a 16-lane group of operand reads covers all 64 banks).
 // Reduction slots: instruction t of a stage takes chunks 2t (lane half 0)
 // and 2t + 1 (half 1) of every row, for A and B alike.  Gate/up multiplies
@@ -1196,6 +1198,7 @@ constexpr int kDnRows = 128;   // rows per block
 constexpr int kDnB = 256;      // weight rows per block
 constexpr int kDnK = 64;       // K per stage
 constexpr int kDnStages = 3;   // stages in LDS
+constexpr int kDnThreads = 512;  // 8 waves: 2 row halves x 4 column groups
 
 template <int MODE>
 constexpr int dense_cols() { return MODE == kModeGateUp ? kDnB / 2 : kDnB; }
@@ -1210,7 +1213,7 @@ struct DenseArgs {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
+__global__ __launch_bounds__(kDnThreads, 1) void k_dense(DenseArgs p) {
   constexpr int kRowU = kDnK / 2;  // dwords per staged row
   constexpr int OP = MODE == kModeGateUp ? kOpBF16 : kOpF16;
   __shared__ __attribute__((aligned(16))) uint32_t s_a[kDnStages][kDnRows * kRowU];
@@ -1223,6 +1226,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
   const int row0 = ti * kDnRows, n0 = bx * dense_cols<MODE>();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wc = wave & 3, rh = wave >> 2;  // column group, row half
   const int l32 = lane & 31, h = lane >> 5;
   const int nk = p.K / kDnK;
 
@@ -1232,8 +1236,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
   const i32x4r_t ra = rsrc_words(p.a, (uint32_t)p.T * (uint32_t)p.K * 2u);
   const uint32_t wb = (uint32_t)p.N * (uint32_t)p.K * 2u;
   const i32x4r_t r0 = rsrc_words(p.w0, wb), r1 = rsrc_words(MODE == kModeGateUp ? p.w1 : p.w0, wb);
-  constexpr int kARuns = kDnRows / 8 / 4;  // A runs per wave and stage: 4
-  constexpr int kBRuns = kDnB / 8 / 4;     // B runs per wave and stage: 8
+  constexpr int kARuns = kDnRows / 8 / 8;  // A runs per wave and stage: 2
+  constexpr int kBRuns = kDnB / 8 / 8;     // B runs per wave and stage: 4
   uint32_t avo[kARuns], bvo[kBRuns];
 #pragma unroll
   for (int u = 0; u < kARuns; u++) {
@@ -1264,9 +1268,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
     }
   };
 
-  f32x16v_t acc[4][2];
+  f32x16v_t acc[2][2];
 #pragma unroll
-  for (int m = 0; m < 4; m++)
+  for (int m = 0; m < 2; m++)
 #pragma unroll
     for (int nb = 0; nb < 2; nb++)
 #pragma unroll
@@ -1276,7 +1280,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
   if (nk > 1) issue(1);
   // stage 0 in LDS for every wave (this wave's stage-1 loads may still fly)
   if (nk > 1)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kARuns + kBRuns));
   else
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
@@ -1285,11 +1289,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
     const uint32_t *A = s_a[it % kDnStages];
     const uint32_t *B = s_b[it % kDnStages];
     auto a_frag = [&](int m, int t) {
-      const int row = 32 * m + l32;
+      const int row = 64 * rh + 32 * m + l32;
       return *reinterpret_cast<const uint4 *>(&A[row * kRowU + 4 * ((2 * t + h) ^ ((row >> 1) & 7))]);
     };
     auto b_frag = [&](int nb, int t) {
-      const int row = MODE == kModeGateUp ? (kDnB / 2) * nb + 32 * wave + l32 : 64 * wave + 32 * nb + l32;
+      const int row = MODE == kModeGateUp ? (kDnB / 2) * nb + 32 * wc + l32 : 64 * wc + 32 * nb + l32;
       const uint4 v =
           *reinterpret_cast<const uint4 *>(&B[row * kRowU + 4 * ((2 * t + h) ^ ((row >> 1) & 7))]);
       if constexpr (MODE == kModeGateUp)
@@ -1304,7 +1308,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
 #pragma unroll
       for (int nb = 0; nb < 2; nb++) bf[nb] = b_frag(nb, t);
 #pragma unroll
-      for (int m = 0; m < 4; m++) {
+      for (int m = 0; m < 2; m++) {
         const uint4 af = a_frag(m, t);
 #pragma unroll
         for (int nb = 0; nb < 2; nb++) acc[m][nb] = mfma32<OP>(af, bf[nb], acc[m][nb]);
@@ -1315,7 +1319,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
       // then for every wave; the barrier also ends this stage's reads of the
       // buffer that stage it + 3 overwrites
       if (it + 2 < nk)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kARuns + kBRuns));
       else
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __syncthreads();
@@ -1324,19 +1328,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_dense(DenseArgs p) {
 
   // result register i: row 8 (i / 4) + 4 h + i % 4 of row block m, column l32
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
+  for (int m = 0; m < 2; m++) {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const int r = row0 + 32 * m + 8 * (i / 4) + 4 * h + (i % 4);
+      const int r = row0 + 64 * rh + 32 * m + 8 * (i / 4) + 4 * h + (i % 4);
       if (r >= p.T) continue;
       if constexpr (MODE == kModeGateUp) {
         const float a = silu_mul(acc[m][0][i], acc[m][1][i]);
-        const int col = n0 + 32 * wave + l32;
+        const int col = n0 + 32 * wc + l32;
         p.a_out[(size_t)r * p.N + (p.a_swap ? swap12(col) : col)] =
             __builtin_bit_cast(uint16_t, (_Float16)a);
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; nb++) p.y_out[(size_t)r * p.N + n0 + 64 * wave + 32 * nb + l32] = acc[m][nb][i];
+        for (int nb = 0; nb < 2; nb++) p.y_out[(size_t)r * p.N + n0 + 64 * wc + 32 * nb + l32] = acc[m][nb][i];
       }
     }
   }
@@ -1595,7 +1599,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
     DenseArgs da{T, H, I, x, reinterpret_cast<const uint16_t *>(gate.data),
                  reinterpret_cast<const uint16_t *>(up.data), a16, nullptr, g.a_swap};
     err = launch(k_dense<kModeGateUp>, dim3(I / dense_cols<kModeGateUp>(), (T + kDnRows - 1) / kDnRows),
-                 dim3(kGemmThreads), s, da);
+                 dim3(kDnThreads), s, da);
   } else {
     err = gemm_fmt<kModeGateUp, BM>(g, gate.fmt, gateup_op(gate.fmt), max_tiles, s, dma);
   }
@@ -1610,7 +1614,7 @@ hipError_t gemm_bm(const WView &gate, const WView &up, const WView &down, int H,
     DenseArgs dd{n_rows, I, H, a16, reinterpret_cast<const uint16_t *>(down.data), nullptr,
                  nullptr, y, 0};
     return launch(k_dense<kModeDown>, dim3(H / dense_cols<kModeDown>(), (n_rows + kDnRows - 1) / kDnRows),
-                  dim3(kGemmThreads), s, dd);
+                  dim3(kDnThreads), s, dd);
   }
   return gemm_fmt<kModeDown, BM>(d, down.fmt, kOpF16, max_tiles, s, dma);
 }
