@@ -330,25 +330,28 @@ __global__ __launch_bounds__(kA8Threads) void k_gemm_a8(A8Args p) {
 }
 
 // ---------------------------------------------------------------------------
-// 128-row tiles with every operand moved into LDS by direct loads (as the
-// dense bf16 GEMM).  A block of 8 waves computes 128 bucket rows of one expert
-// against 256 weight rows: wave (h, c) = (w / 4, w % 4) takes rows 64 h +
-// [0, 64) and the columns of k_gemm_a8's wave c (gate/up: columns 32 c +
-// [0, 32) of gate and of up, one MX-FP8 scale group; down: outputs 64 c +
-// [0, 64)), 4 x 4 accumulators of 16 x 16, which stay in VGPRs at two waves
-// per SIMD.  Each weight byte is staged once per 128 rows.  Three K stages of
-// 128 in LDS:
-//   A codes, 128 rows x 128 bytes, 16-byte chunks XOR-swizzled by
+// Tiles of BM = 128 or 192 rows with every operand moved into LDS by direct
+// loads (as the dense bf16 GEMM).  A block of 8 waves computes BM bucket rows
+// of one expert against 256 weight rows: wave (h, c) = (w / 4, w % 4) takes
+// rows BM/2 h + [0, BM/2) and the columns of k_gemm_a8's wave c (gate/up:
+// columns 32 c + [0, 32) of gate and of up, one MX-FP8 scale group; down:
+// outputs 64 c + [0, 64)), BM/32 x 4 accumulators of 16 x 16, which stay in
+// VGPRs at two waves per SIMD.  Each weight byte is staged once per tile: with
+// 192 rows a bucket of up to 192 rows (prefill 4096: 128 +- 11) reads its
+// expert's weights once.  Three K stages of 128 in LDS:
+//   A codes, BM rows x 128 bytes, 16-byte chunks XOR-swizzled by
 //     (row / 2) % 8; the MFMA's A lane (row r, lane group g) reads chunks g
 //     and 4 + g of its row;
 //   B nibbles, 256 rows x 64 bytes stored chunk-major (chunk g of every row,
 //     then chunk g + 1), so the 16 lanes of a lane group read consecutive
 //     16-byte slots; B lane (column n, group g) reads chunk g of row n;
 //   the E8M0 scale dwords of A and B rows (4 k-blocks of 32 per stage).
-// Every wave issues the same 5 direct loads per stage: 2 runs of A, 2 runs of
-// B and one scale load (waves 0-3: 32 A rows each; waves 4-7: 64 B rows).
-// The loop is compiled once per count of live 16-row blocks of the wave's
-// half (0, 2 or 4; a wave with none still loads and keeps the barriers).
+// Every wave issues the same direct loads per stage, so one vmcnt immediate
+// serves all: BM/64 runs of A, 2 runs of B, and the scales (128: one load,
+// 32 A rows on waves 0-3, 64 B rows on waves 4-7; 192: 24 A rows and 32 B
+// rows on every wave).  The loop is compiled once per count of live 16-row
+// blocks of the wave's half (0, 2, 4, or 6 with 192 rows; a wave with none
+// still loads and keeps the barriers).
 // ---------------------------------------------------------------------------
 constexpr int kA8DmaThreads = 512;
 
