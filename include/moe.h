@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum {
   MOE_OK = 0,
@@ -200,6 +200,28 @@ size_t moe_dispatch_workspace(int T, int E, int k);
 int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_offsets,
                  int32_t *sorted_token, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* moe_check_buckets: validate bucket arrays held in host memory: host
+ * copies of moe_dispatch's outputs, or buckets a caller built for
+ * moe_expert_ffn and moe_combine.  The bucketing is the library's own, as
+ * for moe_dispatch (the pages describe none).
+ *   expert_offsets: int32 [E+1]; it must start at 0, never decrease, and
+ *     end at n_rows.
+ *   sorted_token: int32 [n_rows], each value in [0, T); NULL skips this
+ *     check.
+ *   slot_pos: int32 [T*k] with T*k == n_rows, a permutation of [0, n_rows),
+ *     so that every bucket row is the home of exactly one slot; NULL skips
+ *     this check.
+ * It reads only these arrays and makes no device call.  Returns MOE_OK, or
+ * MOE_EINVAL with a message naming the first index at fault.
+ * A library built with MOE_DEBUG defined runs the same checks before any
+ * launch, on host copies of its device inputs:
+ *   moe_expert_ffn checks expert_offsets and sorted_token;
+ *   moe_combine checks that each slot_pos value lies in [0, T*k).
+ * The copies synchronize the stream, so such a build cannot be captured
+ * in a graph. */
+int moe_check_buckets(int T, int E, int k, int n_rows, const int32_t *expert_offsets,
+                      const int32_t *sorted_token, const int32_t *slot_pos);
 
 /* ---------------------------------------------------------------------- */
 /* moe_expert_ffn: SwiGLU FFN of each expert over its bucket of tokens:

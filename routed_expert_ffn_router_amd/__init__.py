@@ -82,6 +82,7 @@ def lib():
         L.moe_dispatch_workspace.restype = sz
         L.moe_dispatch_workspace.argtypes = [i32, i32, i32]
         L.moe_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_check_buckets.argtypes = [i32, i32, i32, i32, vp, vp, vp]
         L.moe_expert_ffn_workspace.restype = sz
         L.moe_expert_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.moe_expert_ffn.argtypes = [i32, i32, i32, vp, C.POINTER(Weights), C.POINTER(Weights),
@@ -272,6 +273,27 @@ def route(x, w_router, k, mode=ROUTE_SOFTMAX_TOPK, logits_in=None, token_ids=Non
                            _ptr(token_ids), _ptr(idx), _ptr(w), _ptr(lo), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream()))
     return idx, w, lo
+
+
+def check_buckets(T, E, k, n_rows, expert_offsets, sorted_token=None, slot_pos=None):
+    """moe_check_buckets on host int32 arrays (numpy): expert_offsets [E+1],
+    sorted_token [n_rows], slot_pos [T*k]; raises MoeError on a malformed
+    bucketing."""
+    import numpy as np
+
+    def host(a, n, name):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        if a.size != n:
+            raise ValueError(f"{name}: {a.size} values, expected {n}")
+        return a
+
+    off = host(expert_offsets, E + 1, "expert_offsets")
+    st = host(sorted_token, n_rows, "sorted_token")
+    sp = host(slot_pos, T * k, "slot_pos")
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    _check(lib().moe_check_buckets(T, E, k, n_rows, ptr(off), ptr(st), ptr(sp)))
 
 
 def dispatch(topk_idx, E):

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "moe_internal.h"
 
@@ -433,6 +434,50 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
                    "dispatch");
 }
 
+int moe_check_buckets(int T, int E, int k, int n_rows, const int32_t *expert_offsets,
+                      const int32_t *sorted_token, const int32_t *slot_pos) {
+  if (T < 0 || E < 1 || n_rows < 0) return fail(MOE_EINVAL, "bad T = %d, E = %d, n_rows = %d", T, E, n_rows);
+  if (!expert_offsets) return fail(MOE_EINVAL, "null expert_offsets");
+  if (expert_offsets[0] != 0)
+    return fail(MOE_EINVAL, "expert_offsets[0] = %d, not 0", expert_offsets[0]);
+  for (int e = 0; e < E; e++)
+    if (expert_offsets[e + 1] < expert_offsets[e])
+      return fail(MOE_EINVAL, "expert_offsets decreases at %d (%d -> %d)", e,
+                  expert_offsets[e], expert_offsets[e + 1]);
+  if (expert_offsets[E] != n_rows)
+    return fail(MOE_EINVAL, "expert_offsets[E] = %d, not n_rows = %d", expert_offsets[E], n_rows);
+  if (sorted_token)
+    for (int r = 0; r < n_rows; r++)
+      if (sorted_token[r] < 0 || sorted_token[r] >= T)
+        return fail(MOE_EINVAL, "sorted_token[%d] = %d outside [0, %d)", r, sorted_token[r], T);
+  if (slot_pos) {
+    if (k < 1 || (long long)T * k != n_rows)
+      return fail(MOE_EINVAL, "slot_pos needs T * k = n_rows (T = %d, k = %d, n_rows = %d)", T,
+                  k, n_rows);
+    std::vector<char> seen((size_t)n_rows, 0);
+    for (int f = 0; f < n_rows; f++) {
+      const int r = slot_pos[f];
+      if (r < 0 || r >= n_rows)
+        return fail(MOE_EINVAL, "slot_pos[%d] = %d outside [0, %d)", f, r, n_rows);
+      if (seen[r]) return fail(MOE_EINVAL, "slot_pos[%d] = %d repeats an earlier slot's row", f, r);
+      seen[r] = 1;
+    }
+  }
+  return MOE_OK;
+}
+
+#ifdef MOE_DEBUG
+// host copies of device index arrays for the MOE_DEBUG checks (synchronous)
+static int debug_fetch(std::vector<int32_t> &h, const int32_t *d, size_t n, hipStream_t s) {
+  h.resize(n);
+  if (n == 0) return MOE_OK;
+  if (hipMemcpyAsync(h.data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(MOE_EHIP, "MOE_DEBUG: copy of index arrays failed");
+  return MOE_OK;
+}
+#endif
+
 size_t moe_expert_ffn_workspace(int T, int n_rows, int E, int H, int I, int fmt_gate,
                                 int fmt_down, int act_fmt) {
   (void)fmt_gate, (void)fmt_down;
@@ -482,6 +527,14 @@ int moe_expert_ffn(int T, int H, int I, const uint16_t *x, const moe_weights *ga
       moe_expert_ffn_workspace(T, n_rows, E, H, I, gate->fmt, down->fmt, act_fmt);
   if (!ws || ws_bytes < need)
     return fail(MOE_ENOSPC, "expert_ffn workspace: %zu bytes < %zu", ws_bytes, need);
+#ifdef MOE_DEBUG
+  if (!dense) {
+    std::vector<int32_t> ho, hs;
+    MOE_TRY(debug_fetch(ho, expert_offsets, (size_t)E + 1, as_stream(stream)));
+    MOE_TRY(debug_fetch(hs, sorted_token, (size_t)n_rows, as_stream(stream)));
+    MOE_TRY(moe_check_buckets(T, E, 0, n_rows, ho.data(), hs.data(), nullptr));
+  }
+#endif
   Carver c(ws);
   FfnBufs b = carve_ffn(c, T, n_rows, E, H, I, dense, act_fmt);
   return run_ffn(T, H, I, x, view_of(*gate), view_of(*up), view_of(*down), act_fmt,
@@ -498,6 +551,16 @@ int moe_combine(int T, int H, int k, const float *y_rows, const int32_t *slot_po
   if (!aligned(y_rows, 16) || !aligned(out_f32, 16) || (shared_y && !aligned(shared_y, 16)) ||
       (steer_dir && !aligned(steer_dir, 16)) || (out_bf16 && !aligned(out_bf16, 8)))
     return fail(MOE_EINVAL, "combine buffers misaligned");
+#ifdef MOE_DEBUG
+  {
+    std::vector<int32_t> hp;
+    const int n = T * k;
+    MOE_TRY(debug_fetch(hp, slot_pos, (size_t)n, as_stream(stream)));
+    for (int f = 0; f < n; f++)
+      if (hp[f] < 0 || hp[f] >= n)
+        return fail(MOE_EINVAL, "slot_pos[%d] = %d outside [0, %d)", f, hp[f], n);
+  }
+#endif
   return hip_check(launch_combine(T, H, k, y_rows, slot_pos, topk_w, shared_y, steer_dir,
                                   steer_alpha, out_f32, out_bf16, as_stream(stream)),
                    "combine");

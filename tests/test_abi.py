@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
 
 
 def test_library_creates_no_hip_objects():
@@ -229,3 +229,45 @@ def test_binding_refuses_host_tensors():
     _lib()
     with pytest.raises(TypeError):
         moe.dispatch(torch.zeros((4, 2), dtype=torch.int32), 8)
+
+
+def test_check_buckets():
+    """moe_check_buckets (host only) accepts the oracle's dispatch of random
+    and edge-case choices and names the first fault of each planted error."""
+    _lib()
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(3)
+    for T, E, k in [(1, 8, 2), (37, 16, 4), (300, 256, 8), (5, 1024, 16)]:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+        if T > 1:
+            idx[0] = np.arange(k) % E  # distinct choices of token 0; repeats elsewhere
+        off, st, _, sp = oracle.dispatch(idx, E)
+        moe.check_buckets(T, E, k, T * k, off, st, sp)
+        moe.check_buckets(T, E, k, T * k, off)  # offsets alone
+    T, E, k = 37, 16, 4
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    off, st, _, sp = oracle.dispatch(idx, E)
+    n = T * k
+
+    def bad(msg, o=off, s=st, p=sp, nr=n):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.check_buckets(T, E, k, nr, o, s, p)
+        assert ei.value.code == moe.EINVAL and msg in str(ei.value), str(ei.value)
+
+    o = off.copy(); o[0] = 1
+    bad("expert_offsets[0] = 1", o=o)
+    o = off.copy(); e = int(np.argmax(np.diff(off) > 0)); o[e + 1] = o[e] - 1
+    bad(f"expert_offsets decreases at {e}", o=o)
+    bad(f"expert_offsets[E] = {n}, not n_rows = {n + 1}", nr=n + 1, s=np.append(st, 0), p=None)
+    s = st.copy(); s[5] = T
+    bad(f"sorted_token[5] = {T} outside", s=s)
+    s = st.copy(); s[9] = -1
+    bad("sorted_token[9] = -1 outside", s=s)
+    p = sp.copy(); p[7] = n
+    bad(f"slot_pos[7] = {n} outside", p=p)
+    p = sp.copy(); p[11] = p[3]
+    bad("slot_pos[11]", p=p)
+    bad("slot_pos needs T * k = n_rows", nr=n - 1, o=np.minimum(off, n - 1), s=st[:-1])

@@ -185,6 +185,8 @@ def test_dispatch_bit_exact(dev, T, E, k):
     ref = oracle.dispatch(idx, E)
     for g, r, name in zip(got, ref, ["offsets", "sorted_token", "sorted_slot", "slot_pos"]):
         assert np.array_equal(g, r), name
+    # the host-side bucket check accepts the device's bucketing
+    moe.check_buckets(T, E, k, T * k, got[0], got[1], got[3])
 
 
 # --------------------------------------------------------------------------

@@ -5,8 +5,9 @@ Two instrumented builds, each in a temporary directory:
 * the oracle (oracle/moe_oracle.c) with gcc, -fsanitize=address,undefined;
   the oracle's own pin and layer tests then run against it;
 * libmoe with the sanitizers on its host code only (hipcc's device code is
-  built as usual); the ABI tests then run against it: workspace sizing,
-  argument validation and every error path that returns before a HIP call.
+  built as usual) and MOE_DEBUG's host-side index checks compiled in; the
+  ABI tests then run against it: workspace sizing, argument validation,
+  every error path that returns before a HIP call, and moe_check_buckets.
 
 Each suite runs in a child process with the sanitizer runtime preloaded,
 halting on the first report; the child also checks that the instrumented
@@ -83,7 +84,10 @@ def test_libmoe_host_code_under_asan_and_ubsan(tmp_path):
     if not rt:
         pytest.skip("clang's AddressSanitizer runtime is not installed")
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    # MOE_DEBUG: the host-side index checks are compiled in (and under the
+    # sanitizers) as well
     flags = ["--offload-arch=gfx950", "-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17",
+             "-DMOE_DEBUG",
              "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     objs, procs = [], []
