@@ -436,7 +436,8 @@ int moe_dispatch(int T, int E, int k, const int32_t *topk_idx, int32_t *expert_o
 
 int moe_check_buckets(int T, int E, int k, int n_rows, const int32_t *expert_offsets,
                       const int32_t *sorted_token, const int32_t *slot_pos) {
-  if (T < 0 || E < 1 || n_rows < 0) return fail(MOE_EINVAL, "bad T = %d, E = %d, n_rows = %d", T, E, n_rows);
+  if (T < 0 || E < 1 || n_rows < 0)
+    return fail(MOE_EINVAL, "bad T = %d, E = %d, n_rows = %d", T, E, n_rows);
   if (!expert_offsets) return fail(MOE_EINVAL, "null expert_offsets");
   if (expert_offsets[0] != 0)
     return fail(MOE_EINVAL, "expert_offsets[0] = %d, not 0", expert_offsets[0]);
@@ -459,7 +460,8 @@ int moe_check_buckets(int T, int E, int k, int n_rows, const int32_t *expert_off
       const int r = slot_pos[f];
       if (r < 0 || r >= n_rows)
         return fail(MOE_EINVAL, "slot_pos[%d] = %d outside [0, %d)", f, r, n_rows);
-      if (seen[r]) return fail(MOE_EINVAL, "slot_pos[%d] = %d repeats an earlier slot's row", f, r);
+      if (seen[r])
+        return fail(MOE_EINVAL, "slot_pos[%d] = %d repeats an earlier slot's row", f, r);
       seen[r] = 1;
     }
   }
