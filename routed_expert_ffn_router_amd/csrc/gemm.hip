@@ -299,7 +299,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   constexpr int NB = col_blocks<FMT>();
   constexpr int kPA = 4;       // A stages in flight (one group)
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
-  __shared__ uint32_t s_a[2][BM * kLdsRowW];
+  // A stage buffers.  Down: four, two stages written per barrier into the
+  // two buffers the previous two stages read (one barrier per two stages:
+  // decode b16 down 71 -> 67 us); gate/up: two, one barrier per stage (the
+  // two-stage form cost the VQ2 gate/up a wave per SIMD and 1-5%)
+  constexpr int kAB = MODE == kModeDown ? 4 : 2;
+  __shared__ uint32_t s_a[kAB][BM * kLdsRowW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   // XCD-aware block order (block_tile)
   int ti, bx;
@@ -369,10 +374,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) sb16[u][nb].load(*wv[nb], e, wrow[nb], a_k_b16(u, lg));
   }
-  sa[0].store(&s_a[0][arow * kLdsRowW + acol / 2]);
   // stages past the end re-read the last one (never used; keeps the loads unconditional)
-  sa[0].load(ra, a_off, a_kb(min(kPA, nk - 1)), acol);
-  __syncthreads();  // A stage 0 and the codebook
+#pragma unroll
+  for (int u = 0; u < kAB / 2; u++) {
+    sa[u].store(&s_a[u][arow * kLdsRowW + acol / 2]);
+    sa[u].load(ra, a_off, a_kb(min(kPA + u, nk - 1)), acol);
+  }
+  __syncthreads();  // the first A stages and the codebook
 
   const int m_active = (r1 - r0 + 15) >> 4;  // row blocks holding bucket rows
   f32x4v_t acc[MB][NB];
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     for (int S = 0; S < 4; S++) {
       const int it = 4 * G + S;
       // this stage's A fragments, all read before the matrix instructions
-      const uint32_t *A = s_a[it & 1];
+      const uint32_t *A = s_a[it & (kAB - 1)];
       uint4 af[2][MB];
 #pragma unroll
       for (int t = 0; t < 2; t++)
@@ -440,11 +448,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
           }
         }
       }
-      // A: stage it + 1 into the other buffer, refill its slot
-      const int an = (S + 1) & 3;
-      sa[an].store(&s_a[(it + 1) & 1][arow * kLdsRowW + acol / 2]);
-      sa[an].load(ra, a_off, a_kb(min(it + 1 + kPA, nk - 1)), acol);
-      __syncthreads();
+      // A: the next kAB / 2 stages into their buffers (after every stage, or
+      // every second one), their register slots refilled kPA stages on
+      if (kAB == 2 || (S & 1)) {
+#pragma unroll
+        for (int u = 1; u <= kAB / 2; u++) {
+          const int an = (S + u) & 3;
+          sa[an].store(&s_a[(it + u) & (kAB - 1)][arow * kLdsRowW + acol / 2]);
+          sa[an].load(ra, a_off, a_kb(min(it + u + kPA, nk - 1)), acol);
+        }
+        __syncthreads();
+      }
     }
   };
   for (int G = 0; G < ng; G += 2) {
