@@ -294,16 +294,18 @@ __device__ __forceinline__ f32x4v_t mfma16(uint4 a, uint4 b, f32x4v_t c) {
 // the grouped GEMM: grid.x = column blocks of the layer, grid.y = bucket tiles
 // ---------------------------------------------------------------------------
 template <int MODE, int FMT, int OP, int BM>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
+// (16-row gate/up of the decoded formats: at least 3 waves per SIMD, which
+// the two-stage A schedule otherwise exceeds by one register)
+__global__ __launch_bounds__(kGemmThreads, BM == 16 && FMT != MOE_FMT_MXFP4 && MODE == kModeGateUp ? 3 : 1) void k_gemm(GemmArgs p) {
   constexpr int MB = BM / 16;  // MFMA row blocks
   constexpr int NB = col_blocks<FMT>();
   constexpr int kPA = 4;       // A stages in flight (one group)
   constexpr bool kGroupB = FMT != MOE_FMT_BF16;
-  // A stage buffers.  Down: four, two stages written per barrier into the
-  // two buffers the previous two stages read (one barrier per two stages:
-  // decode b16 down 71 -> 67 us); gate/up: two, one barrier per stage (the
-  // two-stage form cost the VQ2 gate/up a wave per SIMD and 1-5%)
-  constexpr int kAB = MODE == kModeDown ? 4 : 2;
+  // A stage buffers: four, two stages written per barrier into the two
+  // buffers the previous two stages read (one barrier per two stages: decode
+  // b16 down 70 -> 66 us, gate/up 94 -> 91 us); MXFP4 gate/up keeps two and
+  // a barrier per stage (its wider raw groups leave no registers for it)
+  constexpr int kAB = MODE == kModeDown || FMT != MOE_FMT_MXFP4 ? 4 : 2;
   __shared__ uint32_t s_a[kAB][BM * kLdsRowW];
   __shared__ uint2 s_cb[FMT == MOE_FMT_VQ2 ? 256 * kNCopy : 1];
   // XCD-aware block order (block_tile)
